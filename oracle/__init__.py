@@ -1,0 +1,9 @@
+"""fp64 CPU oracle for Fibonacci-spaced sparse attention (test infrastructure).
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this package. It shares no code with the HIP library.
+"""
+from .fsa_oracle import (FIB, SCHEDULE_COPRIME, SCHEDULE_FIXED,  # noqa: F401
+                         SCHEDULE_LINEAR, backward, backward_slab, dkdv_rows,
+                         dq_rows, forward, forward_rows, forward_slab,
+                         offset_table, schedule)

@@ -1,0 +1,44 @@
+"""Seeded input generator: determinism, rounding and RoPE properties (CPU)."""
+
+import numpy as np
+
+from static_pattern_sparse_amd import inputs as I
+
+
+def test_deterministic_and_distinct_streams():
+    a = I.make_inputs(1, 2, 64, 16, "bf16", 2, 3)
+    b = I.make_inputs(1, 2, 64, 16, "bf16", 2, 3)
+    c = I.make_inputs(1, 2, 64, 16, "bf16", 2, 4)
+    for n in a:
+        assert np.array_equal(a[n], b[n])
+        assert not np.array_equal(a[n], c[n])
+    assert not np.array_equal(a["q"], a["k"])
+
+
+def test_bf16_values_are_exact_and_nearest():
+    x = np.random.default_rng(0).standard_normal(10000).astype(np.float32)
+    r = I.round_to_bf16(x)
+    assert (r.view(np.uint32) & 0xFFFF == 0).all()
+    # nearest: no other bf16 neighbour is closer
+    up = ((r.view(np.uint32) + 0x10000).view(np.float32))
+    dn = ((r.view(np.uint32) - 0x10000).view(np.float32))
+    e = np.abs(r.astype(np.float64) - x)
+    assert (e <= np.abs(up.astype(np.float64) - x)).all()
+    assert (e <= np.abs(dn.astype(np.float64) - x)).all()
+
+
+def test_rope_is_a_rotation_of_each_pair():
+    T, D = 50, 16
+    raw = I.make_tensor(1, 1, T, D, "f32", 9, 0, "q", rope_base=None)[0, 0]
+    rot = I.make_tensor(1, 1, T, D, "f32", 9, 0, "q", rope_base=10000.0)[0, 0]
+    h = D // 2
+    n_raw = raw[:, :h] ** 2 + raw[:, h:] ** 2
+    n_rot = rot[:, :h] ** 2 + rot[:, h:] ** 2
+    np.testing.assert_allclose(n_rot, n_raw, rtol=1e-5)
+    assert np.array_equal(raw[0], rot[0])          # position 0 is not rotated
+
+
+def test_workload_table_shapes():
+    w = I.WORKLOADS["linear16_bf16_b1h16t65536d128_w12"]
+    assert (w.B, w.H, w.T, w.D, w.rope_base) == (1, 16, 65536, 128, 500000.0)
+    assert len({x.workload_id for x in I.WORKLOADS.values()}) == len(I.WORKLOADS)
