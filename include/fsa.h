@@ -1,0 +1,151 @@
+/*
+ * fsa.h -- C ABI of libfsa, Fibonacci-spaced sparse attention for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Method: "Depth-Staggered Fibonacci Spacing for Sparse Attention" (C. A.
+ * Capps; gist.science technical summary), cited below as [DSFS: <section>].
+ * Each query at position i attends a dense causal window of W keys plus up to
+ * fifteen keys at distances d_k = alpha * f_k, f = 1, 2, 3, 5, ..., 987, with
+ * one scalar alpha per layer in [0.5, 1.5]; a fractional distance linearly
+ * interpolates the two neighbouring key rows and value rows, so the loss has a
+ * gradient with respect to alpha; RoPE is applied before the gather
+ * [DSFS: Methodology > Architecture and attention: Attended set, Scaling,
+ * Implementation]. The schedules are those of [DSFS: Methodology >
+ * Experimental variables].
+ *
+ * Conventions fixed by this library where the page is silent:
+ *   - window: key offsets 0..W-1 (the query itself included), cut at row 0;
+ *   - a tap with alpha*f_k < W is dropped (it lies inside the window);
+ *   - a tap whose position i - alpha*f_k is negative is dropped for query i;
+ *   - tap rows: lower a = i - ceil(alpha*f_k) with weight 1 - t, upper a + 1
+ *     with weight t = ceil(alpha*f_k) - alpha*f_k;
+ *   - one softmax over the union of window and tap entries, scale 1/sqrt(D);
+ *   - alpha is taken as the given fp32 value; the distances are formed in fp64;
+ *   - at an integer distance d(alpha) uses the slope K[a+1] - K[a], V[a+1] - V[a].
+ *
+ * Tensor layout: every q, k, v, dout, out, dq, dk, dv is a dense row-major
+ * [B][H][T][D] array (element (b,h,t,d) at ((b*H + h)*T + t)*D + d); lse is
+ * [B][H][T]. q and k are the post-RoPE rows.
+ *
+ * Memory and streams: every tensor pointer is a DEVICE pointer owned by the
+ * caller; the library allocates no memory and never synchronises. `stream` is
+ * a hipStream_t (NULL = the null stream); work is enqueued on it and the call
+ * returns at once. Outputs are overwritten, never accumulated into.
+ *
+ * Errors: each call returns an fsa_status. Argument checks run before any HIP
+ * call, so an invalid call enqueues nothing. FSA_ERR_HIP means a launch failed;
+ * fsa_last_hip_error() gives the HIP error code of the calling thread. Faults
+ * inside kernels surface later, at the caller's synchronisation.
+ *
+ * Thread safety: the library holds no mutable global state apart from the
+ * thread-local last HIP error; calls from several threads are safe.
+ */
+#ifndef FSA_H_
+#define FSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FSA_OK 0
+#define FSA_ERR_INVALID_ARG 1 /* null/misaligned pointer, bad size, bad alpha */
+#define FSA_ERR_UNSUPPORTED 2 /* head dim or dtype this build has no kernel for */
+#define FSA_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
+#define FSA_ERR_HIP 4         /* a HIP launch failed; see fsa_last_hip_error() */
+
+/* schedules [DSFS: Methodology > Experimental variables] */
+#define FSA_SCHEDULE_FIXED 0   /* alpha = 1 for every layer */
+#define FSA_SCHEDULE_LINEAR 1  /* alpha from alpha_min (layer 0) to alpha_max (last layer) */
+#define FSA_SCHEDULE_COPRIME 2 /* linear values re-assigned by l -> stride*l mod L */
+
+/* element types of q, k, v and dout */
+#define FSA_DTYPE_F32 0
+#define FSA_DTYPE_BF16 1
+
+#define FSA_NUM_TAPS 15 /* Fibonacci distances 1, 2, 3, 5, ..., 987 */
+
+/*
+ * fsa_schedule -- per-layer alpha table, host only.
+ *   kind        FSA_SCHEDULE_*.
+ *   num_layers  L >= 1.
+ *   alpha_min, alpha_max  ends of the linear ladder, 0.5 <= min <= max <= 1.5
+ *               (ignored for FIXED).
+ *   stride      coprime stride, gcd(stride, L) = 1 (COPRIME only; 7 in the page).
+ *   alpha_out   host array of L floats, written.
+ * LINEAR: alpha_l = min + (max - min) * l / (L - 1), evaluated in fp64 and
+ * rounded once to fp32 (alpha_0 = min when L = 1). COPRIME: out[(stride*l) mod L]
+ * = linear[l]. Returns FSA_ERR_INVALID_ARG on a null pointer, L < 1, a range
+ * outside [0.5, 1.5], min > max, or gcd(stride, L) != 1.
+ */
+int fsa_schedule(int kind, int num_layers, float alpha_min, float alpha_max,
+                 int stride, float* alpha_out);
+
+/*
+ * fsa_offsets -- the tap table the kernels use, host only (for inspection).
+ * [DSFS: Methodology > Architecture and attention > Scaling, Implementation]
+ *   alpha     fp32 scale in [0.5, 1.5]; window W >= 1.
+ *   c_out     host int32[15]: ceil(alpha*f_k), distance of the lower row.
+ *   t_out     host float[15]: ceil(alpha*f_k) - alpha*f_k, weight of the upper
+ *             row, rounded to fp32 from the exact fp64 value.
+ *   keep_out  host uint8[15]: 1 when alpha*f_k >= W.
+ * Returns FSA_ERR_INVALID_ARG on a null pointer, W < 1 or a bad alpha.
+ */
+int fsa_offsets(float alpha, int window, int32_t* c_out, float* t_out,
+                uint8_t* keep_out);
+
+/*
+ * fsa_forward -- out, lse of one layer.
+ * [DSFS: Methodology > Architecture and attention]
+ *   q, k, v   device [B][H][T][D] of `dtype` (q, k post-RoPE), 16-byte aligned.
+ *   dtype     FSA_DTYPE_F32 or FSA_DTYPE_BF16.
+ *   B, H, T   >= 0 (a zero product is a no-op); D in {64, 128}.
+ *   alpha     fp32 in [0.5, 1.5]; window W >= 1 (W >= T gives causal attention).
+ *   out       device float [B][H][T][D], written (fp32 for every dtype).
+ *   lse       device float [B][H][T], written: log of the softmax denominator
+ *             (natural log, scores already scaled by 1/sqrt(D)).
+ */
+int fsa_forward(const void* q, const void* k, const void* v, int dtype, int B,
+                int H, int T, int D, float alpha, int window, float* out,
+                float* lse, void* stream);
+
+/*
+ * fsa_backward_workspace_size -- bytes of device scratch fsa_backward needs
+ * (per-row softmax terms and per-tile dalpha partials). Returns 0 for an empty
+ * problem or an unsupported shape.
+ */
+size_t fsa_backward_workspace_size(int B, int H, int T, int D, int dtype);
+
+/*
+ * fsa_backward -- gradients of one layer.
+ * [DSFS: Methodology > Architecture and attention > Implementation (gradient
+ * reaches alpha); Experimental variables > Learned]
+ *   q, k, v, dout  device [B][H][T][D] of `dtype`; dout is dLoss/dout.
+ *   lse       device float [B][H][T] from fsa_forward on the same inputs.
+ *   dq, dk, dv  device float [B][H][T][D], written (gradients w.r.t. the
+ *             post-RoPE q and k, and v).
+ *   dalpha    device float[1], written: dLoss/dalpha summed over B, H and T.
+ *   workspace device scratch of at least fsa_backward_workspace_size() bytes,
+ *             256-byte aligned; its contents on entry do not matter.
+ * The result is deterministic (fixed reduction order).
+ */
+int fsa_backward(const void* q, const void* k, const void* v,
+                 const void* dout, const float* lse, int dtype, int B, int H,
+                 int T, int D, float alpha, int window, float* dq, float* dk,
+                 float* dv, float* dalpha, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* fsa_status_string -- static text for a status code. */
+const char* fsa_status_string(int status);
+
+/* fsa_last_hip_error -- HIP error code of this thread's last FSA_ERR_HIP. */
+int fsa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H_ */

@@ -1,0 +1,48 @@
+// Internal declarations shared by the host planner and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fsa {
+
+constexpr int kNumTaps = 15;
+
+// Kept taps of one layer, ascending distance. Built on the host in fp64 from
+// the fp32 alpha (Depth-Staggered Fibonacci Spacing for Sparse Attention,
+// Methodology > Architecture and attention > Scaling, Implementation) and
+// passed to the kernels by value.
+struct Taps {
+  int n;                   // number of kept taps (d_k >= W)
+  int c[kNumTaps];         // ceil(d_k): distance of the lower row
+  float w_lo[kNumTaps];    // 1 - t_k, weight of the lower row
+  float w_hi[kNumTaps];    // t_k = ceil(d_k) - d_k, weight of the upper row
+  float neg_f[kNumTaps];   // -f_k, d(position)/d(alpha) of the tap
+};
+
+struct Problem {
+  int B, H, T, D, W;
+  float scale;  // 1/sqrt(D)
+};
+
+// Workspace layout of the backward pass (offsets in bytes, 256-aligned).
+struct BwdWorkspace {
+  size_t delta_off;     // float[B*H*T]: Delta_i = sum_e p_ie dP_ie
+  size_t partial_off;   // float[n_partials]: per-tile dalpha partial sums
+  size_t n_partials;
+  size_t total;
+};
+BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype);
+
+// Launchers; each returns the hipError_t of its launch.
+hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
+                          int dtype, const Problem& pr, const Taps& taps,
+                          float* out, float* lse, hipStream_t s);
+hipError_t launch_bwd_vec(const void* q, const void* k, const void* v,
+                          const void* dout, const float* lse, int dtype,
+                          const Problem& pr, const Taps& taps, float* dq,
+                          float* dk, float* dv, float* delta, float* partials,
+                          size_t n_partials, float* dalpha, hipStream_t s);
+
+}  // namespace fsa

@@ -1,0 +1,180 @@
+"""Thin Python binding of libfsa's C ABI (argument marshalling only).
+
+The names mirror the C entry points declared in include/fsa.h. Tensors are
+torch tensors on the GPU; torch supplies device memory and the current stream,
+and every step of the computation runs in libfsa's HIP kernels. There is no
+fallback: if libfsa.so is missing or fails to load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+FSA_OK = 0
+FSA_ERR_INVALID_ARG = 1
+FSA_ERR_UNSUPPORTED = 2
+FSA_ERR_WORKSPACE = 3
+FSA_ERR_HIP = 4
+
+FSA_SCHEDULE_FIXED = 0
+FSA_SCHEDULE_LINEAR = 1
+FSA_SCHEDULE_COPRIME = 2
+
+FSA_DTYPE_F32 = 0
+FSA_DTYPE_BF16 = 1
+
+NUM_TAPS = 15
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsa.so")
+EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_forward",
+           "fsa_backward_workspace_size", "fsa_backward", "fsa_status_string",
+           "fsa_last_hip_error")
+
+_lib = None
+
+
+class FsaError(RuntimeError):
+    def __init__(self, fn, status, lib):
+        msg = lib.fsa_status_string(status).decode()
+        if status == FSA_ERR_HIP:
+            msg += f" (hip error {lib.fsa_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Open libfsa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m static_pattern_sparse_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.fsa_schedule.argtypes = [i32, i32, f32, f32, i32, ctypes.POINTER(f32)]
+    L.fsa_schedule.restype = i32
+    L.fsa_offsets.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_int32),
+                              ctypes.POINTER(f32), ctypes.POINTER(ctypes.c_uint8)]
+    L.fsa_offsets.restype = i32
+    L.fsa_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                              vp, vp, vp]
+    L.fsa_forward.restype = i32
+    L.fsa_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.fsa_backward_workspace_size.restype = ctypes.c_size_t
+    L.fsa_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                               f32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.fsa_backward.restype = i32
+    L.fsa_status_string.argtypes = [i32]
+    L.fsa_status_string.restype = ctypes.c_char_p
+    L.fsa_last_hip_error.argtypes = []
+    L.fsa_last_hip_error.restype = i32
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != FSA_OK:
+        raise FsaError(fn, status, lib())
+
+
+def fsa_schedule(kind, num_layers=16, alpha_min=0.5, alpha_max=1.5, stride=7):
+    out = np.zeros(num_layers, dtype=np.float32)
+    st = lib().fsa_schedule(int(kind), int(num_layers), float(alpha_min),
+                            float(alpha_max), int(stride),
+                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    _check("fsa_schedule", st)
+    return out
+
+
+def fsa_offsets(alpha, window):
+    c = np.zeros(NUM_TAPS, dtype=np.int32)
+    t = np.zeros(NUM_TAPS, dtype=np.float32)
+    keep = np.zeros(NUM_TAPS, dtype=np.uint8)
+    st = lib().fsa_offsets(float(alpha), int(window),
+                           c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                           t.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                           keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    _check("fsa_offsets", st)
+    return c, t, keep.astype(bool)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return FSA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return FSA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, T, D] tensors")
+    for x in (q,):
+        if not x.is_cuda or not x.is_contiguous():
+            raise ValueError("tensors must be contiguous CUDA/HIP tensors")
+    return tuple(int(s) for s in q.shape)
+
+
+def fsa_forward(q, k, v, alpha, window, out=None, lse=None, stream=None):
+    """out [B,H,T,D] fp32 and lse [B,H,T] fp32 of one layer."""
+    import torch
+    B, H, T, D = _shape(q)
+    for x in (k, v):
+        if x.shape != q.shape or x.dtype != q.dtype or not x.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if out is None:
+        out = torch.empty((B, H, T, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    st = lib().fsa_forward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T,
+                           D, float(alpha), int(window), _ptr(out), _ptr(lse),
+                           _stream(stream))
+    _check("fsa_forward", st)
+    return out, lse
+
+
+def fsa_backward_workspace_size(B, H, T, D, dtype_code):
+    return int(lib().fsa_backward_workspace_size(int(B), int(H), int(T), int(D),
+                                                 int(dtype_code)))
+
+
+def fsa_backward(q, k, v, dout, lse, alpha, window, dq=None, dk=None, dv=None,
+                 dalpha=None, workspace=None, stream=None):
+    """dq, dk, dv [B,H,T,D] fp32 and dalpha [1] fp32 of one layer."""
+    import torch
+    B, H, T, D = _shape(q)
+    for x in (k, v, dout):
+        if x.shape != q.shape or x.dtype != q.dtype or not x.is_contiguous():
+            raise ValueError("q, k, v, dout must share shape, dtype and be contiguous")
+    dt = _dtype_code(q)
+    mk = lambda: torch.empty((B, H, T, D), dtype=torch.float32, device=q.device)
+    dq = mk() if dq is None else dq
+    dk = mk() if dk is None else dk
+    dv = mk() if dv is None else dv
+    if dalpha is None:
+        dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
+    nbytes = fsa_backward_workspace_size(B, H, T, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), dt,
+                            B, H, T, D, float(alpha), int(window), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(),
+                            _stream(stream))
+    _check("fsa_backward", st)
+    return dq, dk, dv, dalpha

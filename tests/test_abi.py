@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: exports, host tables, argument validation.
+
+Only calls that return before any HIP call are made here (host-only entry
+points, and compute entry points with arguments the validation rejects).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import fsa_oracle as O
+from static_pattern_sparse_amd import fsa as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH),
+                                reason="libfsa.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    lib = ctypes.CDLL(F.LIB_PATH)
+    names = _declared()
+    assert "fsa_forward" in names and "fsa_backward" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(F.EXPORTS)
+
+
+@pytest.mark.parametrize("kind", [F.FSA_SCHEDULE_FIXED, F.FSA_SCHEDULE_LINEAR,
+                                  F.FSA_SCHEDULE_COPRIME])
+@pytest.mark.parametrize("L", [1, 2, 5, 16, 17])
+def test_schedule_bit_exact_vs_oracle(kind, L):
+    if kind == F.FSA_SCHEDULE_COPRIME and np.gcd(7, L) != 1:
+        with pytest.raises(F.FsaError):
+            F.fsa_schedule(kind, L)
+        return
+    got = F.fsa_schedule(kind, L)
+    ref = O.schedule(kind, L)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("alpha", list(O.schedule(O.SCHEDULE_LINEAR, 16)) + [0.7317, 1.2913])
+@pytest.mark.parametrize("W", [1, 6, 12, 100])
+def test_offsets_vs_oracle(alpha, W):
+    c, t, keep = F.fsa_offsets(alpha, W)
+    d_r, c_r, t_r, keep_r = O.offset_table(alpha, W)
+    assert np.array_equal(c, c_r)
+    assert np.array_equal(keep, keep_r)
+    assert np.array_equal(t, t_r.astype(np.float32))
+
+
+def test_schedule_validation():
+    with pytest.raises(F.FsaError):
+        F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 0)
+    with pytest.raises(F.FsaError):
+        F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 16, alpha_min=0.4)
+    with pytest.raises(F.FsaError):
+        F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 16, alpha_min=1.2, alpha_max=1.0)
+    with pytest.raises(F.FsaError):
+        F.fsa_schedule(F.FSA_SCHEDULE_COPRIME, 16, stride=6)
+    with pytest.raises(F.FsaError):
+        F.fsa_schedule(9, 16)
+    with pytest.raises(F.FsaError):
+        F.fsa_offsets(1.6, 8)
+    with pytest.raises(F.FsaError):
+        F.fsa_offsets(1.0, 0)
+    with pytest.raises(F.FsaError):
+        F.fsa_offsets(float("nan"), 8)
+
+
+FAKE = 0x7f0000000000   # never dereferenced: validation fails first
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, B=1, H=1, T=16, D=64, alpha=1.0,
+             W=4, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return F.lib().fsa_forward(*(ctypes.c_void_p(a[n]) if n in ("q", "k", "v", "out", "lse")
+                                 else a[n] for n in ("q", "k", "v", "dtype", "B", "H", "T",
+                                                     "D", "alpha", "W", "out", "lse")), None)
+
+
+def test_forward_validation_codes():
+    assert _fwd(alpha=1.6) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(alpha=0.49) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(alpha=float("inf")) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(W=0) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(T=-1) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(D=96) == F.FSA_ERR_UNSUPPORTED
+    assert _fwd(D=32) == F.FSA_ERR_UNSUPPORTED
+    assert _fwd(dtype=5) == F.FSA_ERR_UNSUPPORTED
+    assert _fwd(q=0) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(lse=0) == F.FSA_ERR_INVALID_ARG
+    assert _fwd(k=FAKE + 2) == F.FSA_ERR_INVALID_ARG       # misaligned
+    assert _fwd(B=300, H=300) == F.FSA_ERR_UNSUPPORTED       # too many heads
+    # an empty problem is a no-op that touches nothing
+    assert _fwd(T=0, q=0, k=0, v=0, out=0, lse=0) == F.FSA_OK
+    assert _fwd(B=0) == F.FSA_OK
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, lse=FAKE, dtype=1, B=1, H=1, T=16,
+             D=64, alpha=1.0, W=4, dq=FAKE, dk=FAKE, dv=FAKE, da=FAKE, ws=FAKE,
+             nbytes=1 << 20)
+    a.update(kw)
+    ptr = ("q", "k", "v", "g", "lse", "dq", "dk", "dv", "da", "ws")
+    order = ("q", "k", "v", "g", "lse", "dtype", "B", "H", "T", "D", "alpha", "W",
+             "dq", "dk", "dv", "da", "ws", "nbytes")
+    return F.lib().fsa_backward(*(ctypes.c_void_p(a[n]) if n in ptr else a[n]
+                                  for n in order), None)
+
+
+def test_backward_validation_codes():
+    assert _bwd(alpha=2.0) == F.FSA_ERR_INVALID_ARG
+    assert _bwd(da=0) == F.FSA_ERR_INVALID_ARG
+    assert _bwd(g=0) == F.FSA_ERR_INVALID_ARG
+    assert _bwd(dv=FAKE + 4) == F.FSA_ERR_INVALID_ARG
+    assert _bwd(D=80) == F.FSA_ERR_UNSUPPORTED
+    assert _bwd(ws=0) == F.FSA_ERR_WORKSPACE
+    assert _bwd(nbytes=16) == F.FSA_ERR_WORKSPACE
+    assert _bwd(ws=FAKE + 16) == F.FSA_ERR_WORKSPACE         # not 256-aligned
+
+
+def test_workspace_size():
+    n = F.fsa_backward_workspace_size(8, 8, 1024, 64, F.FSA_DTYPE_BF16)
+    assert n >= 8 * 8 * 1024 * 4 and n % 256 == 0
+    assert F.fsa_backward_workspace_size(0, 8, 1024, 64, 1) == 0
+    assert F.fsa_backward_workspace_size(1, 1, 16, 96, 1) == 0
+    big = F.fsa_backward_workspace_size(1, 16, 65536, 128, 1)
+    assert big >= 16 * 65536 * 4
