@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Fibonacci-spaced sparse attention: forward + backward throughput on one MI355X.
+
+One step = forward (out, lse) and backward (dq, dk, dv, dalpha) of every layer
+of a 16-layer linear-stagger stack, B=8, H=8, T=1024, D=64, W=12, bf16 inputs
+(the page's 16-layer, 8x64-wide model at its 1024-token training length;
+Depth-Staggered Fibonacci Spacing for Sparse Attention, Methodology). Each
+layer has its own input and output buffers (about 1.5 GiB in all, more than the
+256 MB Infinity Cache), so a layer's data is not cached from one step to the
+next. Inputs are seeded N(0,1) synthetic tensors (post-RoPE q, k) and sit in
+HBM before the timed region starts.
+
+value = layers * B * H * T / step time (token-heads per second, every layer
+counted). The JSON line also carries:
+  roofline      the dominant kernel's algorithmic bytes per launch divided by
+                its mean launch time (HIP events on the launch stream), against
+                the 8 TB/s HBM peak; traffic from committed rocprofv3 counter
+                summaries when they match the current kernel source, else null;
+  cpu_baseline  the fp64 oracle on the host cores over the same step;
+  t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "Fib-sparse attn fwd+bwd tokens·heads/s and % peak HBM GB/s at T=1024/4096"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "static_pattern_sparse_amd", "csrc", n)
+                  for n in ("fsa_vec.hip", "fsa_mfma.hip")]
+
+
+def stage_bytes(D, in_bytes):
+    """Algorithmic HBM bytes per token-head of every kernel: each tensor the
+    kernel must read or write, once."""
+    row_in = D * in_bytes
+    return {
+        "fwd": 3 * row_in + 4 * D + 4,                 # q k v -> out lse
+        "bwd_dq": 4 * row_in + 4 + 4 * D + 4,          # q k v dout lse -> dq delta
+        "bwd_dkdv": 4 * row_in + 8 + 8 * D,            # q k v dout lse delta -> dk dv
+    }
+
+
+def algo_bytes(D, in_bytes):
+    """Algorithmic bytes per token-head of the forward and of the backward as
+    a whole (each input read once, each output written once)."""
+    row_in = D * in_bytes
+    return {"fwd": 3 * row_in + 4 * D + 4,
+            "bwd": 4 * row_in + 4 + 12 * D}
+
+
+class Stack:
+    """Device buffers of every layer of one workload."""
+
+    def __init__(self, wl, window, layers, torch, F, I):
+        self.torch, self.F = torch, F
+        self.wl, self.W, self.layers = wl, window, layers
+        kind = {"linear": F.FSA_SCHEDULE_LINEAR, "coprime": F.FSA_SCHEDULE_COPRIME,
+                "fixed": F.FSA_SCHEDULE_FIXED}[wl.schedule]
+        self.alphas = F.fsa_schedule(kind, wl.layers)
+        B, H, T, D = wl.B, wl.H, wl.T, wl.D
+        dev = "cuda"
+        self.L = []
+        ws_bytes = F.fsa_backward_workspace_size(B, H, T, D, F.FSA_DTYPE_BF16)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        for l in range(layers):
+            x = I.workload_inputs(wl, l)
+            t = {n: I.to_device(x[n], wl.dtype) for n in ("q", "k", "v", "dout")}
+            f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+            t.update(out=f32(B, H, T, D), lse=f32(B, H, T), dq=f32(B, H, T, D),
+                     dk=f32(B, H, T, D), dv=f32(B, H, T, D), dalpha=f32(1))
+            self.L.append(t)
+        self.host = None
+
+    def step(self, ev=None):
+        F = self.F
+        for l, t in enumerate(self.L):
+            a = float(self.alphas[l])
+            rec = (lambda name: ev.record(name)) if ev else (lambda name: None)
+            rec("fwd")
+            F.fsa_forward(t["q"], t["k"], t["v"], a, self.W, out=t["out"], lse=t["lse"])
+            rec("bwd_dq")
+            F.fsa_backward_dq(t["q"], t["k"], t["v"], t["dout"], t["lse"], a, self.W,
+                              t["dq"], self.ws)
+            rec("bwd_dkdv")
+            F.fsa_backward_dkdv(t["q"], t["k"], t["v"], t["dout"], t["lse"], a, self.W,
+                                t["dk"], t["dv"], self.ws)
+            rec("dalpha")
+            F.fsa_backward_dalpha(t["q"], t["dalpha"], self.ws)
+            rec(None)
+
+
+class Events:
+    """Back-to-back HIP events on the launch stream; the time between the
+    event recorded before a launch and the next event is that launch's time."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def record(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.torch.cuda.current_stream())
+        self.marks.append((name, e))
+
+    def per_kernel_ms(self):
+        tot, cnt = {}, {}
+        for (name, e0), (_, e1) in zip(self.marks, self.marks[1:]):
+            if name is None:
+                continue
+            tot[name] = tot.get(name, 0.0) + e0.elapsed_time(e1)
+            cnt[name] = cnt.get(name, 0) + 1
+        return {n: tot[n] / cnt[n] for n in tot}, cnt
+
+
+def time_stack(stack, steps, warmup, torch):
+    for _ in range(warmup):
+        stack.step()
+    torch.cuda.synchronize()
+    ev = Events(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stack.step(ev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    per_ms, counts = ev.per_kernel_ms()
+    return ms_step, per_ms, counts
+
+
+def summarise(stack, ms_step, per_ms):
+    wl = stack.wl
+    th = wl.B * wl.H * wl.T                      # token-heads per layer call
+    in_b = 2 if wl.dtype == "bf16" else 4
+    sb = stage_bytes(wl.D, in_b)
+    ab = algo_bytes(wl.D, in_b)
+    kernels = {}
+    for n, ms in per_ms.items():
+        k = {"mean_us": round(ms * 1e3, 3)}
+        if n in sb:
+            gbs = sb[n] * th / (ms * 1e-3) / 1e9
+            k.update(bytes_per_launch=sb[n] * th, gbs=round(gbs, 1),
+                     hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        kernels[n] = k
+    fwd_ms = per_ms["fwd"]
+    bwd_ms = per_ms["bwd_dq"] + per_ms["bwd_dkdv"] + per_ms["dalpha"]
+    frac = {
+        "fwd": round(ab["fwd"] * th / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bwd": round(ab["bwd"] * th / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "fwd_bwd": round((ab["fwd"] + ab["bwd"]) * th / ((fwd_ms + bwd_ms) * 1e-3)
+                         / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    value = stack.layers * th / (ms_step * 1e-3)
+    return value, kernels, frac
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, per_launch_tokens):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of the
+    kernel, when it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_digest:\s*(\w+)", text)
+    b = re.search(r"hbm_bytes_per_token_head:\s*([0-9.eE+-]+)", text)
+    if not m or not b or m.group(1) != source_digest():
+        return None
+    return float(b.group(1)) * per_launch_tokens
+
+
+# ------------------------------------------------------------- CPU baseline
+def _oracle_layer(args):
+    import numpy as np
+    from oracle import fsa_oracle as O
+    q, k, v, g, alpha, W = args
+    B, H = q.shape[:2]
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            sl = [x[b, h].astype(np.float64) for x in (q, k, v, g)]
+            O.forward_slab(sl[0], sl[1], sl[2], alpha, W)
+            O.backward_slab(sl[0], sl[1], sl[2], sl[3], alpha, W)
+    return time.perf_counter() - t0
+
+
+def _noop(_):
+    return os.getpid()
+
+
+def cpu_baseline(wl, window, alphas, layers):
+    """The fp64 oracle (forward + backward of every (b, h) slab) over whole
+    layers of the workload, one layer per worker task."""
+    from static_pattern_sparse_amd import inputs as I
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    jobs = []
+    for l in range(layers):
+        x = I.workload_inputs(wl, l)
+        jobs.append((x["q"], x["k"], x["v"], x["dout"], float(alphas[l]), window))
+    ctx = multiprocessing.get_context("spawn")
+    from concurrent.futures import ProcessPoolExecutor
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        list(ex.map(_noop, range(workers * 2)))          # start every worker
+        t0 = time.perf_counter()
+        busy = list(ex.map(_oracle_layer, jobs))
+        wall = time.perf_counter() - t0
+    th = layers * wl.B * wl.H * wl.T
+    return {"value": round(th / wall, 1), "unit": "tokens·heads/s",
+            "cores": workers, "kind": "oracle",
+            "sample": (f"{layers} layers x {wl.B * wl.H} (b,h) slabs of {wl.name}, "
+                       f"forward+backward in fp64 numpy, {workers} spawned "
+                       f"single-threaded workers; {wall:.1f} s wall, "
+                       f"{sum(busy):.1f} s CPU")}
+
+
+# ------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-t4096", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(the heads shard with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from static_pattern_sparse_amd import fsa as F
+    from static_pattern_sparse_amd import inputs as I
+    torch.cuda.set_device(0)
+    F.lib()
+
+    wl = I.WORKLOADS["linear16_bwd_bf16_b8h8t1024d64_w12"]
+    stack = Stack(wl, 12, args.layers, torch, F, I)
+    print(f"[bench] {wl.name}: {args.layers} layers resident", file=sys.stderr, flush=True)
+    ms_step, per_ms, counts = time_stack(stack, args.steps, args.warmup, torch)
+    value, kernels, frac = summarise(stack, ms_step, per_ms)
+    print(f"[bench] {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    dom = max((n for n in per_ms if n != "dalpha"), key=lambda n: per_ms[n])
+    th = wl.B * wl.H * wl.T
+    achieved = kernels[dom]["gbs"]
+    traffic = load_traffic(dom, th)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": kernels[dom]["bytes_per_launch"],
+                "mean_launch_us": kernels[dom]["mean_us"]}
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens·heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) post-RoPE q, k; v; dout)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "D": wl.D,
+                   "W": 12, "layers": args.layers, "schedule": wl.schedule,
+                   "pass": "forward+backward"},
+        "roofline": roofline,
+        "hbm_frac": frac,
+        "kernels": kernels,
+        "launches_per_kernel": counts,
+    }
+    del stack
+    torch.cuda.empty_cache()
+
+    if not args.skip_t4096:
+        wl2 = I.WORKLOADS["coprime16_bf16_b4h8t4096d64_w6-12"]
+        st2 = Stack(wl2, 12, args.layers, torch, F, I)
+        print(f"[bench] {wl2.name} W=12 resident", file=sys.stderr, flush=True)
+        ms2, per2, _ = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
+        v2, k2, f2 = summarise(st2, ms2, per2)
+        res["t4096"] = {"workload": wl2.name + " (W=12)", "value": round(v2, 1),
+                        "ms_per_step": round(ms2, 4), "hbm_frac": f2, "kernels": k2}
+        del st2
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, 12, F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 16),
+                                           args.layers)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,56 @@ int check_shape(int dtype, int B, int H, int T, int D, float alpha, int window) 
   return FSA_OK;
 }
 
+Problem make_problem(int B, int H, int T, int D, int window) {
+  return Problem{B, H, T, D, window,
+                 static_cast<float>(1.0 / std::sqrt(static_cast<double>(D)))};
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FSA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return FSA_ERR_HIP;
+}
+
+struct BwdArgs {
+  bool empty = false;
+  Problem pr{};
+  Taps taps{};
+  float* delta = nullptr;
+  float* partials = nullptr;
+};
+
+BwdWorkspace bwd_layout(int B, int H, int T, int D, int dtype);
+
+// Checks shared by the backward stages; fills *a on success.
+int check_bwd(const void* q, const void* k, const void* v, const void* dout,
+              const float* lse, int dtype, int B, int H, int T, int D,
+              float alpha, int window, void* workspace, size_t workspace_bytes,
+              BwdArgs* a) {
+  int st = check_shape(dtype, B, H, T, D, alpha, window);
+  if (st != FSA_OK) return st;
+  a->empty = static_cast<long long>(B) * H * T == 0;
+  if (a->empty) return FSA_OK;
+  if (!q || !k || !v || !dout || !lse) return FSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+      !aligned16(lse))
+    return FSA_ERR_INVALID_ARG;
+  const BwdWorkspace ws = bwd_layout(B, H, T, D, dtype);
+  if (workspace == nullptr || workspace_bytes < ws.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FSA_ERR_WORKSPACE;
+  build_taps(alpha, window, &a->taps);
+  a->pr = make_problem(B, H, T, D, window);
+  char* wsb = static_cast<char*>(workspace);
+  a->delta = reinterpret_cast<float*>(wsb + ws.delta_off);
+  a->partials = reinterpret_cast<float*>(wsb + ws.partial_off);
+  return FSA_OK;
+}
+
+BwdWorkspace bwd_layout(int B, int H, int T, int D, int dtype) {
+  return bwd_workspace_layout(B, H, T, D, dtype);
+}
+
 }  // namespace
 
 BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
@@ -81,6 +131,35 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
   w.partial_off = align256(rows * sizeof(float));
   w.total = align256(w.partial_off + w.n_partials * sizeof(float));
   return w;
+}
+
+// Kernel family per dtype: fp32 inputs take the lane-per-row kernels.
+hipError_t launch_forward(const void* q, const void* k, const void* v,
+                          int dtype, const Problem& pr, const Taps& taps,
+                          float* out, float* lse, hipStream_t s) {
+  return launch_fwd_vec(q, k, v, dtype, pr, taps, out, lse, s);
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, int dtype,
+                         const Problem& pr, const Taps& taps, float* dq,
+                         float* delta, float* partials, hipStream_t s) {
+  return launch_bwd_dq_vec(q, k, v, dout, lse, dtype, pr, taps, dq, delta,
+                           partials, s);
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse,
+                           const float* delta, int dtype, const Problem& pr,
+                           const Taps& taps, float* dk, float* dv,
+                           hipStream_t s) {
+  return launch_bwd_dkdv_vec(q, k, v, dout, lse, delta, dtype, pr, taps, dk,
+                             dv, s);
+}
+
+size_t bwd_partials_used(const Problem& pr, int dtype) {
+  (void)dtype;
+  return bwd_partials_used_vec(pr);
 }
 
 }  // namespace fsa
@@ -145,14 +224,9 @@ int fsa_forward(const void* q, const void* k, const void* v, int dtype, int B,
     return FSA_ERR_INVALID_ARG;
   Taps taps;
   build_taps(alpha, window, &taps);
-  Problem pr{B, H, T, D, window, static_cast<float>(1.0 / std::sqrt(double(D)))};
-  hipError_t e = launch_fwd_vec(q, k, v, dtype, pr, taps, out, lse,
-                                static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = static_cast<int>(e);
-    return FSA_ERR_HIP;
-  }
-  return FSA_OK;
+  const Problem pr = make_problem(B, H, T, D, window);
+  return hip_status(launch_forward(q, k, v, dtype, pr, taps, out, lse,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 size_t fsa_backward_workspace_size(int B, int H, int T, int D, int dtype) {
@@ -161,43 +235,77 @@ size_t fsa_backward_workspace_size(int B, int H, int T, int D, int dtype) {
   return bwd_workspace_layout(B, H, T, D, dtype).total;
 }
 
+int fsa_backward_dq(const void* q, const void* k, const void* v,
+                    const void* dout, const float* lse, int dtype, int B, int H,
+                    int T, int D, float alpha, int window, float* dq,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  BwdArgs a;
+  int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
+                     workspace, workspace_bytes, &a);
+  if (st != FSA_OK || a.empty) return st;
+  if (!dq || !aligned16(dq)) return FSA_ERR_INVALID_ARG;
+  return hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
+                                  a.delta, a.partials,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int fsa_backward_dkdv(const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, int dtype, int B,
+                      int H, int T, int D, float alpha, int window, float* dk,
+                      float* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  BwdArgs a;
+  int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
+                     workspace, workspace_bytes, &a);
+  if (st != FSA_OK || a.empty) return st;
+  if (!dk || !dv || !aligned16(dk) || !aligned16(dv)) return FSA_ERR_INVALID_ARG;
+  return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, dtype, a.pr,
+                                    a.taps, dk, dv,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float* dalpha,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(dtype, B, H, T, D, 1.0f, 1);
+  if (st != FSA_OK) return st;
+  if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (static_cast<long long>(B) * H * T == 0)
+    return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
+  const BwdWorkspace ws = bwd_workspace_layout(B, H, T, D, dtype);
+  if (workspace == nullptr || workspace_bytes < ws.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FSA_ERR_WORKSPACE;
+  const Problem pr = make_problem(B, H, T, D, 1);
+  const float* partials = reinterpret_cast<const float*>(
+      static_cast<const char*>(workspace) + ws.partial_off);
+  return hip_status(launch_dalpha_reduce(partials, bwd_partials_used(pr, dtype),
+                                         dalpha, s));
+}
+
 int fsa_backward(const void* q, const void* k, const void* v,
                  const void* dout, const float* lse, int dtype, int B, int H,
                  int T, int D, float alpha, int window, float* dq, float* dk,
                  float* dv, float* dalpha, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  int st = check_shape(dtype, B, H, T, D, alpha, window);
+  BwdArgs a;
+  int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
+                     workspace, workspace_bytes, &a);
   if (st != FSA_OK) return st;
   if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
-  const bool empty = static_cast<long long>(B) * H * T == 0;
-  if (!empty) {
-    if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv)
-      return FSA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
-        !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-      return FSA_ERR_INVALID_ARG;
-  }
-  BwdWorkspace ws{};
-  if (!empty) {
-    ws = bwd_workspace_layout(B, H, T, D, dtype);
-    if (workspace == nullptr || workspace_bytes < ws.total ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return FSA_ERR_WORKSPACE;
-  }
-  Taps taps;
-  build_taps(alpha, window, &taps);
-  Problem pr{B, H, T, D, window, static_cast<float>(1.0 / std::sqrt(double(D)))};
-  char* wsb = static_cast<char*>(workspace);
-  float* delta = empty ? nullptr : reinterpret_cast<float*>(wsb + ws.delta_off);
-  float* partials = empty ? nullptr : reinterpret_cast<float*>(wsb + ws.partial_off);
-  hipError_t e = launch_bwd_vec(q, k, v, dout, lse, dtype, pr, taps, dq, dk, dv,
-                                delta, partials, ws.n_partials, dalpha,
-                                static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = static_cast<int>(e);
-    return FSA_ERR_HIP;
-  }
-  return FSA_OK;
+  if (!a.empty && (!dq || !dk || !dv || !aligned16(dq) || !aligned16(dk) ||
+                   !aligned16(dv)))
+    return FSA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.empty) return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
+  st = hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
+                                a.delta, a.partials, s));
+  if (st != FSA_OK) return st;
+  st = hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, dtype, a.pr,
+                                  a.taps, dk, dv, s));
+  if (st != FSA_OK) return st;
+  return hip_status(launch_dalpha_reduce(
+      a.partials, bwd_partials_used(a.pr, dtype), dalpha, s));
 }
 
 const char* fsa_status_string(int status) {

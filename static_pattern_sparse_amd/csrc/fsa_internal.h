@@ -35,14 +35,39 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype);
 
-// Launchers; each returns the hipError_t of its launch.
+// Launchers; each returns the hipError_t of its launch. The kernel family is
+// chosen from dtype: fp32 inputs use the lane-per-row kernels, bf16 inputs the
+// MFMA tile kernels.
+hipError_t launch_forward(const void* q, const void* k, const void* v,
+                          int dtype, const Problem& pr, const Taps& taps,
+                          float* out, float* lse, hipStream_t s);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, int dtype,
+                         const Problem& pr, const Taps& taps, float* dq,
+                         float* delta, float* partials, hipStream_t s);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse,
+                           const float* delta, int dtype, const Problem& pr,
+                           const Taps& taps, float* dk, float* dv,
+                           hipStream_t s);
+// number of dalpha partials the dq stage writes for this problem
+size_t bwd_partials_used(const Problem& pr, int dtype);
+hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
+                                hipStream_t s);
+
+// lane-per-row kernels (fsa_vec.hip)
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
                           float* out, float* lse, hipStream_t s);
-hipError_t launch_bwd_vec(const void* q, const void* k, const void* v,
-                          const void* dout, const float* lse, int dtype,
-                          const Problem& pr, const Taps& taps, float* dq,
-                          float* dk, float* dv, float* delta, float* partials,
-                          size_t n_partials, float* dalpha, hipStream_t s);
+hipError_t launch_bwd_dq_vec(const void* q, const void* k, const void* v,
+                             const void* dout, const float* lse, int dtype,
+                             const Problem& pr, const Taps& taps, float* dq,
+                             float* delta, float* partials, hipStream_t s);
+hipError_t launch_bwd_dkdv_vec(const void* q, const void* k, const void* v,
+                               const void* dout, const float* lse,
+                               const float* delta, int dtype,
+                               const Problem& pr, const Taps& taps, float* dk,
+                               float* dv, hipStream_t s);
+size_t bwd_partials_used_vec(const Problem& pr);
 
 }  // namespace fsa

@@ -343,27 +343,30 @@ hipError_t fwd_vec_typed(const void* q, const void* k, const void* v,
 }
 
 template <typename Tin, int D>
-hipError_t bwd_vec_typed(const void* q, const void* k, const void* v,
-                         const void* dout, const float* lse, const Problem& pr,
-                         const Taps& taps, float* dq, float* dk, float* dv,
-                         float* delta, float* partials, size_t n_partials,
-                         float* dalpha, hipStream_t s) {
+hipError_t bwd_dq_vec_typed(const void* q, const void* k, const void* v,
+                            const void* dout, const float* lse,
+                            const Problem& pr, const Taps& taps, float* dq,
+                            float* delta, float* partials, hipStream_t s) {
   dim3 grid((pr.T + kVecBlock - 1) / kVecBlock, pr.B * pr.H);
-  const size_t used = static_cast<size_t>(grid.x) * grid.y;
-  if (used > n_partials) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dq_vec_kernel<Tin, D>), grid, dim3(kVecBlock), 0, s,
                      static_cast<const Tin*>(q), static_cast<const Tin*>(k),
                      static_cast<const Tin*>(v), static_cast<const Tin*>(dout),
                      lse, pr, taps, dq, delta, partials);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <typename Tin, int D>
+hipError_t bwd_dkdv_vec_typed(const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse,
+                              const float* delta, const Problem& pr,
+                              const Taps& taps, float* dk, float* dv,
+                              hipStream_t s) {
+  dim3 grid((pr.T + kVecBlock - 1) / kVecBlock, pr.B * pr.H);
   hipLaunchKernelGGL((bwd_dkdv_vec_kernel<Tin, D>), grid, dim3(kVecBlock), 0, s,
                      static_cast<const Tin*>(q), static_cast<const Tin*>(k),
                      static_cast<const Tin*>(v), static_cast<const Tin*>(dout),
                      lse, delta, pr, taps, dk, dv);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_dalpha_reduce(partials, used, dalpha, s);
+  return hipGetLastError();
 }
 }  // namespace
 
@@ -378,21 +381,31 @@ hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                     : fwd_vec_typed<uint16_t, 128>(q, k, v, pr, taps, out, lse, s);
 }
 
-hipError_t launch_bwd_vec(const void* q, const void* k, const void* v,
-                          const void* dout, const float* lse, int dtype,
-                          const Problem& pr, const Taps& taps, float* dq,
-                          float* dk, float* dv, float* delta, float* partials,
-                          size_t n_partials, float* dalpha, hipStream_t s) {
-  if (pr.B * pr.H * pr.T == 0)
-    return launch_dalpha_reduce(partials, 0, dalpha, s);
-  if (dtype == FSA_DTYPE_F32) {
-    return pr.D == 64
-               ? bwd_vec_typed<float, 64>(q, k, v, dout, lse, pr, taps, dq, dk, dv, delta, partials, n_partials, dalpha, s)
-               : bwd_vec_typed<float, 128>(q, k, v, dout, lse, pr, taps, dq, dk, dv, delta, partials, n_partials, dalpha, s);
-  }
-  return pr.D == 64
-             ? bwd_vec_typed<uint16_t, 64>(q, k, v, dout, lse, pr, taps, dq, dk, dv, delta, partials, n_partials, dalpha, s)
-             : bwd_vec_typed<uint16_t, 128>(q, k, v, dout, lse, pr, taps, dq, dk, dv, delta, partials, n_partials, dalpha, s);
+size_t bwd_partials_used_vec(const Problem& pr) {
+  return static_cast<size_t>((pr.T + kVecBlock - 1) / kVecBlock) * pr.B * pr.H;
+}
+
+hipError_t launch_bwd_dq_vec(const void* q, const void* k, const void* v,
+                             const void* dout, const float* lse, int dtype,
+                             const Problem& pr, const Taps& taps, float* dq,
+                             float* delta, float* partials, hipStream_t s) {
+  if (dtype == FSA_DTYPE_F32)
+    return pr.D == 64 ? bwd_dq_vec_typed<float, 64>(q, k, v, dout, lse, pr, taps, dq, delta, partials, s)
+                      : bwd_dq_vec_typed<float, 128>(q, k, v, dout, lse, pr, taps, dq, delta, partials, s);
+  return pr.D == 64 ? bwd_dq_vec_typed<uint16_t, 64>(q, k, v, dout, lse, pr, taps, dq, delta, partials, s)
+                    : bwd_dq_vec_typed<uint16_t, 128>(q, k, v, dout, lse, pr, taps, dq, delta, partials, s);
+}
+
+hipError_t launch_bwd_dkdv_vec(const void* q, const void* k, const void* v,
+                               const void* dout, const float* lse,
+                               const float* delta, int dtype,
+                               const Problem& pr, const Taps& taps, float* dk,
+                               float* dv, hipStream_t s) {
+  if (dtype == FSA_DTYPE_F32)
+    return pr.D == 64 ? bwd_dkdv_vec_typed<float, 64>(q, k, v, dout, lse, delta, pr, taps, dk, dv, s)
+                      : bwd_dkdv_vec_typed<float, 128>(q, k, v, dout, lse, delta, pr, taps, dk, dv, s);
+  return pr.D == 64 ? bwd_dkdv_vec_typed<uint16_t, 64>(q, k, v, dout, lse, delta, pr, taps, dk, dv, s)
+                    : bwd_dkdv_vec_typed<uint16_t, 128>(q, k, v, dout, lse, delta, pr, taps, dk, dv, s);
 }
 
 }  // namespace fsa
