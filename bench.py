@@ -85,37 +85,64 @@ class Stack:
             t.update(out=f32(B, H, T, D), lse=f32(B, H, T), dq=f32(B, H, T, D),
                      dk=f32(B, H, T, D), dv=f32(B, H, T, D), dalpha=f32(1))
             self.L.append(t)
-        self.host = None
+        self._prepare_calls(torch, F)
+
+    def _prepare_calls(self, torch, F):
+        """Pre-marshal every launch of a step (raw ctypes argument tuples), so
+        the host enqueues far faster than the GPU drains."""
+        import ctypes
+        lib = F.lib()
+        vp, f32 = ctypes.c_void_p, ctypes.c_float
+        wl = self.wl
+        B, H, T, D = wl.B, wl.H, wl.T, wl.D
+        dt = F.FSA_DTYPE_BF16 if wl.dtype == "bf16" else F.FSA_DTYPE_F32
+        stream = vp(torch.cuda.current_stream().cuda_stream)
+        ws, nws = vp(self.ws.data_ptr()), self.ws.numel()
+        self.calls = []
+        for l, t in enumerate(self.L):
+            p = {n: vp(x.data_ptr()) for n, x in t.items()}
+            a = f32(float(self.alphas[l]))
+            self.calls.append([
+                ("fwd", lib.fsa_forward, (p["q"], p["k"], p["v"], dt, B, H, T, D, a,
+                                          self.W, p["out"], p["lse"], stream)),
+                ("bwd_dq", lib.fsa_backward_dq, (p["q"], p["k"], p["v"], p["dout"],
+                                                 p["lse"], dt, B, H, T, D, a, self.W,
+                                                 p["dq"], ws, nws, stream)),
+                ("bwd_dkdv", lib.fsa_backward_dkdv, (p["q"], p["k"], p["v"], p["dout"],
+                                                     p["lse"], dt, B, H, T, D, a,
+                                                     self.W, p["dk"], p["dv"], ws, nws,
+                                                     stream)),
+                ("dalpha", lib.fsa_backward_dalpha, (dt, B, H, T, D, a, self.W,
+                                                     p["dalpha"], ws, nws, stream)),
+            ])
 
     def step(self, ev=None):
-        F = self.F
-        for l, t in enumerate(self.L):
-            a = float(self.alphas[l])
-            rec = (lambda name: ev.record(name)) if ev else (lambda name: None)
-            rec("fwd")
-            F.fsa_forward(t["q"], t["k"], t["v"], a, self.W, out=t["out"], lse=t["lse"])
-            rec("bwd_dq")
-            F.fsa_backward_dq(t["q"], t["k"], t["v"], t["dout"], t["lse"], a, self.W,
-                              t["dq"], self.ws)
-            rec("bwd_dkdv")
-            F.fsa_backward_dkdv(t["q"], t["k"], t["v"], t["dout"], t["lse"], a, self.W,
-                                t["dk"], t["dv"], self.ws)
-            rec("dalpha")
-            F.fsa_backward_dalpha(t["q"], t["dalpha"], self.ws)
-            rec(None)
+        for layer_calls in self.calls:
+            for name, fn, args in layer_calls:
+                if ev is not None:
+                    ev.record(name)
+                st = fn(*args)
+                if st != 0:
+                    raise RuntimeError(f"{name} returned status {st}")
+            if ev is not None:
+                ev.record(None)
 
 
 class Events:
     """Back-to-back HIP events on the launch stream; the time between the
-    event recorded before a launch and the next event is that launch's time."""
+    event recorded before a launch and the next event is that launch's time.
+    All events are created up front, so recording one costs the host only the
+    enqueue."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, count):
         self.torch = torch
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
         self.marks = []
+        self.stream = torch.cuda.current_stream()
 
     def record(self, name):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(self.torch.cuda.current_stream())
+        e = self.pool[len(self.marks)]
+        e.record(self.stream)
         self.marks.append((name, e))
 
     def per_kernel_ms(self):
@@ -131,8 +158,7 @@ class Events:
 def time_stack(stack, steps, warmup, torch):
     for _ in range(warmup):
         stack.step()
-    torch.cuda.synchronize()
-    ev = Events(torch)
+    ev = Events(torch, steps * len(stack.calls) * (len(stack.calls[0]) + 1))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):

@@ -157,8 +157,9 @@ int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                       int H, int T, int D, float alpha, int window, float* dk,
                       float* dv, void* workspace, size_t workspace_bytes,
                       void* stream);
-int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float* dalpha,
-                        void* workspace, size_t workspace_bytes, void* stream);
+int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float alpha,
+                        int window, float* dalpha, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* fsa_status_string -- static text for a status code. */
 const char* fsa_status_string(int status);

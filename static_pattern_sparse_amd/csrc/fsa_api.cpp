@@ -133,10 +133,13 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
   return w;
 }
 
-// Kernel family per dtype: fp32 inputs take the lane-per-row kernels.
+// Kernel family: bf16 inputs with a window of at most 33 keys take the MFMA
+// tile kernels; fp32 inputs and wider windows take the lane-per-row kernels.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
                           float* out, float* lse, hipStream_t s) {
+  if (mfma_supported(pr, dtype))
+    return launch_fwd_mfma(q, k, v, pr, taps, out, lse, s);
   return launch_fwd_vec(q, k, v, dtype, pr, taps, out, lse, s);
 }
 
@@ -144,6 +147,8 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, int dtype,
                          const Problem& pr, const Taps& taps, float* dq,
                          float* delta, float* partials, hipStream_t s) {
+  if (mfma_supported(pr, dtype))
+    return launch_bwd_dq_mfma(q, k, v, dout, lse, pr, taps, dq, delta, partials, s);
   return launch_bwd_dq_vec(q, k, v, dout, lse, dtype, pr, taps, dq, delta,
                            partials, s);
 }
@@ -153,13 +158,15 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
                            const float* delta, int dtype, const Problem& pr,
                            const Taps& taps, float* dk, float* dv,
                            hipStream_t s) {
+  if (mfma_supported(pr, dtype))
+    return launch_bwd_dkdv_mfma(q, k, v, dout, lse, delta, pr, taps, dk, dv, s);
   return launch_bwd_dkdv_vec(q, k, v, dout, lse, delta, dtype, pr, taps, dk,
                              dv, s);
 }
 
 size_t bwd_partials_used(const Problem& pr, int dtype) {
-  (void)dtype;
-  return bwd_partials_used_vec(pr);
+  return mfma_supported(pr, dtype) ? bwd_partials_used_mfma(pr)
+                                   : bwd_partials_used_vec(pr);
 }
 
 }  // namespace fsa
@@ -264,9 +271,10 @@ int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                                     static_cast<hipStream_t>(stream)));
 }
 
-int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float* dalpha,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_shape(dtype, B, H, T, D, 1.0f, 1);
+int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float alpha,
+                        int window, float* dalpha, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = check_shape(dtype, B, H, T, D, alpha, window);
   if (st != FSA_OK) return st;
   if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -276,7 +284,7 @@ int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float* dalpha,
   if (workspace == nullptr || workspace_bytes < ws.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FSA_ERR_WORKSPACE;
-  const Problem pr = make_problem(B, H, T, D, 1);
+  const Problem pr = make_problem(B, H, T, D, window);
   const float* partials = reinterpret_cast<const float*>(
       static_cast<const char*>(workspace) + ws.partial_off);
   return hip_status(launch_dalpha_reduce(partials, bwd_partials_used(pr, dtype),

@@ -70,4 +70,20 @@ hipError_t launch_bwd_dkdv_vec(const void* q, const void* k, const void* v,
                                float* dv, hipStream_t s);
 size_t bwd_partials_used_vec(const Problem& pr);
 
+// MFMA tile kernels (fsa_mfma.hip): bf16 inputs, D in {64, 128}, W <= 33
+bool mfma_supported(const Problem& pr, int dtype);
+hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
+                           const Problem& pr, const Taps& taps, float* out,
+                           float* lse, hipStream_t s);
+hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse,
+                              const Problem& pr, const Taps& taps, float* dq,
+                              float* delta, float* partials, hipStream_t s);
+hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
+                                const void* dout, const float* lse,
+                                const float* delta, const Problem& pr,
+                                const Taps& taps, float* dk, float* dv,
+                                hipStream_t s);
+size_t bwd_partials_used_mfma(const Problem& pr);
+
 }  // namespace fsa

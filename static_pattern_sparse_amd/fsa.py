@@ -75,7 +75,7 @@ def lib():
     L.fsa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
     L.fsa_backward_dkdv.restype = i32
-    L.fsa_backward_dalpha.argtypes = [i32, i32, i32, i32, i32, vp, vp,
+    L.fsa_backward_dalpha.argtypes = [i32, i32, i32, i32, i32, f32, i32, vp, vp,
                                       ctypes.c_size_t, vp]
     L.fsa_backward_dalpha.restype = i32
     L.fsa_status_string.argtypes = [i32]
@@ -218,10 +218,11 @@ def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, workspace,
     _check("fsa_backward_dkdv", st)
 
 
-def fsa_backward_dalpha(q, dalpha, workspace, stream=None):
+def fsa_backward_dalpha(q, alpha, window, dalpha, workspace, stream=None):
     """Stage 3 of the backward pass: dalpha[0] from the stage-1 partials."""
     B, H, T, D = _shape(q)
-    st = lib().fsa_backward_dalpha(_dtype_code(q), B, H, T, D, _ptr(dalpha),
+    st = lib().fsa_backward_dalpha(_dtype_code(q), B, H, T, D, float(alpha),
+                                   int(window), _ptr(dalpha),
                                    _ptr(workspace), _ws_bytes(workspace),
                                    _stream(stream))
     _check("fsa_backward_dalpha", st)

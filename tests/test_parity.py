@@ -120,6 +120,9 @@ SMALL = [
     (1, 2, 250, 64, "bf16", 1.0, 300),          # W > T: causal attention
     (1, 1, 200, 128, "f32", 0.8333333, 12),
     (1, 1, 64, 64, "bf16", 1.0, 1),
+    (1, 2, 700, 64, "bf16", 0.6333333, 33),     # widest window of the tile kernels
+    (1, 1, 700, 128, "bf16", 0.6333333, 34),    # first window past them
+    (2, 1, 29, 64, "bf16", 1.1, 2),
 ]
 
 
@@ -142,6 +145,27 @@ def test_forward_deterministic_bitwise():
     g1 = gpu_backward(x, "bf16", 0.7317, 8, l1)
     g2 = gpu_backward(x, "bf16", 0.7317, 8, l1)
     for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_split_phase_backward_matches_fused():
+    torch = _torch()
+    from static_pattern_sparse_amd import fsa as F
+    _say("split phase")
+    x = _rand_inputs(1, 3, 500, 64, "bf16", 5)
+    q, k, v, g = (I.to_device(x[n], "bf16") for n in ("q", "k", "v", "dout"))
+    alpha, W = 0.9, 10
+    _, lse = F.fsa_forward(q, k, v, alpha, W)
+    ref = F.fsa_backward(q, k, v, g, lse, alpha, W)
+    ws = torch.empty(F.fsa_backward_workspace_size(1, 3, 500, 64, F.FSA_DTYPE_BF16),
+                     dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.full_like(ref[0], float("nan")) for _ in range(3))
+    da = torch.full((1,), float("nan"), device="cuda")
+    F.fsa_backward_dq(q, k, v, g, lse, alpha, W, dq, ws)
+    F.fsa_backward_dkdv(q, k, v, g, lse, alpha, W, dk, dv, ws)
+    F.fsa_backward_dalpha(q, alpha, W, da, ws)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv, da), ref):
         assert torch.equal(a, b)
 
 
