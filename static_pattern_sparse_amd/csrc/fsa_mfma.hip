@@ -89,6 +89,14 @@ __device__ __forceinline__ void split_hi_lo(const float* p, u32x4* hi, u32x4* lo
   *lo = __builtin_bit_cast(u32x4, l);
 }
 
+// Order the LDS accesses of one wavefront (its lanes exchange data through
+// LDS; LDS requests of a wavefront complete in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Map the 1-D workgroup id to (head, tile). Workgroups are dispatched
 // round-robin over the 8 XCDs; when the head count allows, all tiles of one
 // head go to one XCD, in order, so the rows its taps re-read stay in that
@@ -168,13 +176,282 @@ __device__ __forceinline__ u32x4 t_operand(const char* lds, int mb, int n, int g
   return a;
 }
 
+// ---------------------------------------------------------------- buffer access
+// Every (b, h) slab is read through a buffer resource that covers exactly the
+// slab (T*D bf16). Offsets outside it -- rows before 0 or at or past T -- read
+// as zero by the hardware range check, so no row index needs clamping.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Keep a byte offset whole in the VGPR operand: a constant part folded into
+// the instruction's immediate field would be checked together with a negative
+// VGPR part, so a row >= 0 reached from a negative block start is loaded with
+// its full offset instead.
+__device__ __forceinline__ int whole(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ uint2 bld8(rsrc_t r, int off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, whole(off), 0, 0);
+  return make_uint2(x[0], x[1]);
+}
+
+// Cross-row (g) sum and max of the 4 lanes l, l^16, l^32, l^48 with the
+// gfx950 row-swap permutes: after permlane16_swap(x, x) the two results hold
+// x[l] and x[l^16] in some order, likewise x[l^32] for permlane32_swap.
+__device__ __forceinline__ float rsum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float rmax4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Hardware exp2 / log2 (v_exp_f32, v_log_f32). Arguments below -126 give
+// denormal results that flush to zero; here they are softmax weights below
+// 2^-126 of the largest, which do not change a sum in fp32.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 hi/lo split: hi = p truncated to bf16, lo = bf16(p - hi). The pair
+// carries p to about 2^-16 relative.
+__device__ __forceinline__ void split8(const float* p, u32x4* hi, u32x4* lo) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    r[e] = p[e] - __uint_as_float(__float_as_uint(p[e]) & 0xffff0000u);
+  u32x4 h;
+  bf16x8 l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    h[e] = __builtin_amdgcn_perm(__float_as_uint(p[2 * e + 1]), __float_as_uint(p[2 * e]), 0x07060302u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) l[e] = static_cast<__bf16>(r[e]);
+  *hi = h;
+  *lo = __builtin_bit_cast(u32x4, l);
+}
+
+// A/B operand rows of a 16-row block starting at row0: lane (g, n) reads row
+// row0 + n, bytes 16g.. of each 64-byte k-step. `lane_a` = n*2D + 16g.
+template <int D>
+__device__ __forceinline__ void bload_rows(rsrc_t r, int lane_a, int row0, u32x4* a) {
+  const int off = lane_a + row0 * (2 * D);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) a[s] = bld16(r, off + 64 * s);
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 mfma_rows(const u32x4* a, const u32x4* b) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) acc = mfma(a[s], b[s], acc);
+  return acc;
+}
+
+// The 4x4 patches of V (or any row tensor) that lane (cc, rg) stages for a
+// 16-row block: rows row0 + 4rg + i, columns 4cc..4cc+3 (+64h).
+// `lane_v` = 4rg*2D + 8cc.
+template <int D>
+__device__ __forceinline__ void bload_patch(rsrc_t r, int lane_v, int row0, uint2 (*p)[4]) {
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[h][i] = bld8(r, lane_v + (row0 + i) * (2 * D) + 128 * h);
+}
+
+// Transpose the patch in registers and write it into half `half` of an LDS
+// pair buffer laid out [d][32 rows] with kLdsRowBytes per d.
+// `lane_w` = 4cc*kLdsRowBytes + 8rg.
+template <int D>
+__device__ __forceinline__ void write_patch(char* lds, int lane_w, int half,
+                                            const uint2 (*p)[4]) {
+  const uint32_t lo = 0x05040100u, hi = 0x07060302u;
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    const uint2* r = p[h];
+    char* w = lds + lane_w + 32 * half + h * 64 * kLdsRowBytes;
+    *reinterpret_cast<uint2*>(w) = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, lo),
+                                              __builtin_amdgcn_perm(r[3].x, r[2].x, lo));
+    *reinterpret_cast<uint2*>(w + kLdsRowBytes) = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, hi),
+                                                             __builtin_amdgcn_perm(r[3].x, r[2].x, hi));
+    *reinterpret_cast<uint2*>(w + 2 * kLdsRowBytes) = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, lo),
+                                                                 __builtin_amdgcn_perm(r[3].y, r[2].y, lo));
+    *reinterpret_cast<uint2*>(w + 3 * kLdsRowBytes) = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, hi),
+                                                                 __builtin_amdgcn_perm(r[3].y, r[2].y, hi));
+  }
+}
+
+__device__ __forceinline__ void zero_patch(uint2 (*p)[4], int nh) {
+  for (int h = 0; h < nh; ++h)
+    for (int i = 0; i < 4; ++i) p[h][i] = make_uint2(0u, 0u);
+}
+
+// A operand X^T of a product over rows, d-block mb: lane (g, n) reads d-row
+// 16mb + n, rows 4g..4g+3 of block X and of block Y. `lane_t` = n*kLdsRowBytes + 8g.
+__device__ __forceinline__ u32x4 lds_operand(const char* lds, int lane_t, int mb) {
+  const char* row = lds + lane_t + mb * 16 * kLdsRowBytes;
+  const uint2 x = *reinterpret_cast<const uint2*>(row);
+  const uint2 y = *reinterpret_cast<const uint2*>(row + 32);
+  u32x4 a;
+  a[0] = x.x; a[1] = x.y; a[2] = y.x; a[3] = y.y;
+  return a;
+}
+
+// Per-lane constants of the 16x16 C layout: lane (g, n) holds rows 4g..4g+3 of
+// column n. For a tap block, query column n takes row n with weight 1-t and
+// row n+1 with weight t; mlo/mhi mark which of the lane's 4 rows those are.
+struct LaneMasks {
+  float mlo[4], mhi[4];
+};
+
+__device__ __forceinline__ LaneMasks lane_masks(int n, int g) {
+  LaneMasks m;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m.mlo[j] = (4 * g + j == n) ? 1.f : 0.f;
+    m.mhi[j] = (4 * g + j == n + 1) ? 1.f : 0.f;
+  }
+  return m;
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A 16-row block of a row tensor (q, k, v or dout of one slab) is staged in
+// LDS row-major, 2D bytes per row, by fully coalesced 16-byte direct-to-LDS
+// buffer loads (lane l of a load writes bytes 16l.. of the load's 1 KB).
+// Within row r the 16-byte chunk c sits at position c ^ swz(r), with
+//   swz(r) = ((r & 3) << 1) | ((r >> 2) & 1),
+// which keeps both read patterns free of bank conflicts:
+//   natural operand  ds_read_b128, lane (g, n): row n, chunk g + 4s
+//                    (8 consecutive rows hit 8 distinct chunk slots);
+//   transposed       ds_read_b64_tr_b16, 16-lane group g: rows 4g'..4g'+3,
+//                    two chunks each (4 rows x 2 chunks -> 8 distinct slots).
+// ds_read_b64_tr_b16: within a 16-lane group, lane i receives element
+// i % 4 of the 8 bytes that lane 4e + i/4 points at, for e = 0..3. With lane j
+// pointing at row k0 + j/4, columns 16mb + 4(j%4)..+3, lane i receives
+// X[k0 + e][16mb + i], e = 0..3: four consecutive rows of one column -- the
+// A operand of a product over rows.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+struct Tile {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  static constexpr int kBlockBytes = 16 * kRowBytes;   // 16 rows
+  static constexpr int kLoads = kBlockBytes / 1024;    // 1 KB per wave load
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+};
+
+// Per-lane byte offsets, fixed for the whole kernel.
+template <int D>
+struct TileLane {
+  int src[Tile<D>::kLoads];   // global offset (w.r.t. the block's first row)
+  int nat[D / 32];            // natural operand read, k-step s
+  int tr[D / 16];             // transposed read, d-block mb (rows 4g..4g+3)
+};
+
+template <int D>
+__device__ __forceinline__ TileLane<D> tile_lane(int lane) {
+  using Tl = Tile<D>;
+  TileLane<D> t;
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ii = 0; ii < Tl::kLoads; ++ii) {
+    const int flat = ii * 1024 + 16 * lane;            // LDS byte in the block
+    const int r = flat / Tl::kRowBytes;
+    const int pos = (flat % Tl::kRowBytes) / 16;
+    t.src[ii] = r * Tl::kRowBytes + 16 * (pos ^ swz(r));
+  }
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    t.nat[s] = n * Tl::kRowBytes + 16 * ((g + 4 * s) ^ swz(n));
+  const int row = 4 * g + (n >> 2);
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb)
+    t.tr[mb] = row * Tl::kRowBytes + 16 * ((2 * mb + ((n & 3) >> 1)) ^ swz(row)) + 8 * (n & 1);
+  return t;
+}
+
+// Issue the loads of rows row0..row0+15 into the LDS block at `dst`. Rows
+// outside the slab are not read (buffer range check).
+template <int D>
+__device__ __forceinline__ void stage_block(rsrc_t r, const TileLane<D>& tl,
+                                            int row0, lds_char* dst) {
+  using Tl = Tile<D>;
+#pragma unroll
+  for (int ii = 0; ii < Tl::kLoads; ++ii)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, dst + ii * 1024, 16, whole(row0 * Tl::kRowBytes + tl.src[ii]), 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void nat_operand(const lds_char* blk, const TileLane<D>& tl,
+                                            u32x4* a) {
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    a[s] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(blk + tl.nat[s]);
+}
+
+// A operand X^T for d-block mb over a pair of blocks (x rows 4g..4g+3 then y).
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const lds_char* x, const lds_char* y,
+                                            const TileLane<D>& tl, int mb) {
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(x + tl.tr[mb]));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(y + tl.tr[mb]));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  u32x4 r;
+  r[0] = ua.x; r[1] = ua.y; r[2] = ub.x; r[3] = ub.y;
+  return r;
+}
+
+// Zero an LDS region (so that rows never loaded read as 0, not as stale
+// bit patterns).
+__device__ __forceinline__ void zero_lds(lds_char* p, int bytes, int lane) {
+  for (int off = 16 * lane; off < bytes; off += 1024)
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p + off) = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Wait until at most n vector-memory loads of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------- forward
+// One wavefront per 15-query tile. Key blocks are taken in pairs (window pairs
+// first, then tap pairs); K and V of the next pair are in flight while the
+// current pair is processed. Softmax is online over the pairs: running max m
+// and sum l (log2 units), the partial output rescaled when m grows.
 template <int D>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Problem pr, Taps taps, int n_tiles,
     float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char lds[D * kLdsRowBytes];
+  using Tl = Tile<D>;
+  constexpr int kStage = 4 * Tl::kBlockBytes;         // K_x K_y V_x V_y
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
   const int n = lane & 15, g = lane >> 4;
   const int T = pr.T, W = pr.W;
@@ -182,141 +459,155 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   map_tile(blockIdx.x, pr.B * pr.H, n_tiles, &bh, &tile);
   const int i0 = tile * kTileQ;
   const size_t base = static_cast<size_t>(bh) * T * D;
-  const uint16_t* Q = q + base;
-  const uint16_t* K = k + base;
-  const uint16_t* V = v + base;
-  const int i = i0 + n;                                  // this lane's query
+  const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
+  const rsrc_t rq = make_rsrc(q + base, slab);
+  const rsrc_t rk = make_rsrc(k + base, slab);
+  const rsrc_t rv = make_rsrc(v + base, slab);
+  const TileLane<D> tl = tile_lane<D>(lane);
+  const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
-
-  u32x4 qb[D / 32];
-  {
-    const uint16_t* p = Q + static_cast<size_t>(clampi(i, 0, T - 1)) * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) qb[s] = ld16(p + 32 * s);
-  }
-  const float scale = pr.scale;
-  const int nwb = (W + kTileQ - 1) / 16 + 1;             // window blocks in use
-  // taps some query of the tile reaches
+  const float c2 = pr.scale * kLog2e;                 // scores in log2 units
+  const LaneMasks lm = lane_masks(n, g);
+  const int nwb = (W + kTileQ - 1) / 16 + 1;
   const int last = min(i0 + kTileQ - 1, T - 1);
   int ntap = 0;
   while (ntap < taps.n && taps.c[ntap] <= last) ++ntap;
+  const int nwp = (nwb + 1) / 2;
+  const int npair = nwp + (ntap + 1) / 2;
 
-  // ---- scores
-  float sw[kMaxWinBlocks][4];
-  float st[kNumTaps];
-  float m = -INFINITY;
-#pragma unroll
-  for (int b = 0; b < kMaxWinBlocks; ++b) {
-    if (b < nwb) {
-      const f32x4 s = score_block<D>(K, i0 - 16 * b, T, qb, n, g);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rel = 4 * g + j - 16 * b;              // key - i0
-        const bool ok = qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
-        sw[b][j] = ok ? s[j] * scale : -INFINITY;
-        m = fmaxf(m, sw[b][j]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sw[b][j] = -INFINITY;
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < kNumTaps; ++t) {
-    st[t] = -INFINITY;
-    if (t < ntap) {
-      const int c = taps.c[t];
-      const f32x4 s = score_block<D>(K, i0 - c, T, qb, n, g);
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = 4 * g + j;
-        part += key == n ? taps.w_lo[t] * s[j] : 0.f;
-        part += key == n + 1 ? taps.w_hi[t] * s[j] : 0.f;
-      }
-      const float sc = xsum4(part) * scale;
-      st[t] = (qvalid && i >= c) ? sc : -INFINITY;
-      m = fmaxf(m, st[t]);
-    }
-  }
-  m = xmax4(m);
-  const float mm = m == -INFINITY ? 0.f : m;
-  float zw = 0.f;
-#pragma unroll
-  for (int b = 0; b < kMaxWinBlocks; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zw += __expf(sw[b][j] - mm);
-  float z = xsum4(zw);
-#pragma unroll
-  for (int t = 0; t < kNumTaps; ++t) z += __expf(st[t] - mm);
-  const float L = qvalid ? mm + __logf(z) : 0.f;
+  zero_lds(lds, 2 * kStage, lane);
+  __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
 
-  // ---- P.V over pairs of key blocks: window blocks first, then taps
+  // rows of block hf of pair p (INT_MIN: no block)
+  auto block_row = [&](int p, int hf) -> int {
+    if (p < nwp) {
+      const int b = 2 * p + hf;
+      return b < nwb ? i0 - 16 * b : INT_MIN;
+    }
+    const int t = 2 * (p - nwp) + hf;
+    return t < ntap ? i0 - taps.c[t] : INT_MIN;
+  };
+  auto stage_pair = [&](int p, lds_char* st) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r0 = block_row(p, hf);
+      if (r0 != INT_MIN) {
+        stage_block<D>(rk, tl, r0, st + hf * Tl::kBlockBytes);
+        stage_block<D>(rv, tl, r0, st + (2 + hf) * Tl::kBlockBytes);
+      }
+    }
+  };
+
+  u32x4 qb[D / 32];
+  bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
+  stage_pair(0, lds);
+
   f32x4 acc[D / 16];
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nblk = nwb + ntap;
-  for (int pb = 0; pb < nblk; pb += 2) {
-    float pv[8];
-    int rows[2];
+  float m = -INFINITY, l = 0.f;
+
+  for (int p = 0; p < npair; ++p) {
+    lds_char* st = lds + (p & 1) * kStage;
+    if (p + 1 < npair) {
+      stage_pair(p + 1, lds + ((p + 1) & 1) * kStage);
+      wait_vm<4 * Tl::kLoads>();                      // this pair's loads done
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- scores of the pair
+    float sv[2][4];
+    float lmax = -INFINITY;
+    const bool win = p < nwp;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int blk = pb + hf;
-      if (blk >= nblk) {
-        rows[hf] = INT_MIN;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pv[4 * hf + j] = 0.f;
-      } else if (blk < nwb) {
-        rows[hf] = i0 - 16 * blk;
-        // select the window block's scores (blk is wave-uniform)
+      for (int j = 0; j < 4; ++j) sv[hf][j] = -INFINITY;
+      const int r0 = block_row(p, hf);
+      if (r0 == INT_MIN) continue;
+      u32x4 ka[D / 32];
+      nat_operand<D>(st + hf * Tl::kBlockBytes, tl, ka);
+      const f32x4 s = mfma_rows<D>(ka, qb);
+      if (win) {
+        const int b = 2 * p + hf;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float s = sw[0][j];
-#pragma unroll
-          for (int b = 1; b < kMaxWinBlocks; ++b) s = blk == b ? sw[b][j] : s;
-          pv[4 * hf + j] = __expf(s - L);
+          const int rel = 4 * g + j - 16 * b;          // key - i0
+          const bool ok = qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
+          sv[hf][j] = ok ? s[j] * c2 : -INFINITY;
+          lmax = fmaxf(lmax, sv[hf][j]);
         }
       } else {
-        const int t = blk - nwb;
-        float s = st[0], wl = taps.w_lo[0], wh = taps.w_hi[0];
-        int c = taps.c[0];
-#pragma unroll
-        for (int u = 1; u < kNumTaps; ++u) {
-          if (t == u) { s = st[u]; wl = taps.w_lo[u]; wh = taps.w_hi[u]; c = taps.c[u]; }
-        }
-        rows[hf] = i0 - c;
-        const float p = __expf(s - L);
+        const int t = 2 * (p - nwp) + hf;
+        float slo = 0.f, shi = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int key = 4 * g + j;
-          pv[4 * hf + j] = key == n ? p * wl : (key == n + 1 ? p * wh : 0.f);
+          slo = fmaf(lm.mlo[j], s[j], slo);
+          shi = fmaf(lm.mhi[j], s[j], shi);
         }
+        const float sc = rsum4(taps.w_lo[t] * slo + taps.w_hi[t] * shi) * c2;
+        sv[hf][0] = (qvalid && i >= taps.c[t]) ? sc : -INFINITY;
+        lmax = fmaxf(lmax, sv[hf][0]);
       }
     }
-    __syncthreads();
-    stage_t<D>(V, rows[0], T, lds, 0, lane);
-    stage_t<D>(V, rows[1], T, lds, 1, lane);
-    __syncthreads();
+    // ---- online softmax update
+    lmax = rmax4(lmax);
+    const float mn = fmaxf(m, lmax);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float corr = ex2(m - ms);                    // 0 when m = -inf
+    float pv[8];
+    float ladd = 0.f;
+    if (win) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pv[4 * hf + j] = ex2(sv[hf][j] - ms);
+          ladd += pv[4 * hf + j];
+        }
+      ladd = rsum4(ladd);
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int t = 2 * (p - nwp) + hf;
+        const int tt = t < ntap ? t : 0;
+        const float pt = ex2(sv[hf][0] - ms);
+        ladd += pt;
+        const float a = pt * taps.w_lo[tt], bb = pt * taps.w_hi[tt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[4 * hf + j] = a * lm.mlo[j] + bb * lm.mhi[j];
+      }
+    }
+    l = l * corr + ladd;
+    m = mn;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[mb][j] *= corr;
+    // ---- P.V of the pair
     u32x4 bhi, blo;
-    split_hi_lo(pv, &bhi, &blo);
+    split8(pv, &bhi, &blo);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 a = t_operand(lds, mb, n, g);
+      const u32x4 a = tr_operand<D>(st + 2 * Tl::kBlockBytes, st + 3 * Tl::kBlockBytes, tl, mb);
       acc[mb] = mfma(a, bhi, acc[mb]);
       acc[mb] = mfma(a, blo, acc[mb]);
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                // reads of stage done
+    __builtin_amdgcn_wave_barrier();
   }
 
   if (qvalid) {
+    const float inv = 1.f / l;
     float* o = out + base + static_cast<size_t>(i) * D + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb)
       *reinterpret_cast<float4*>(o + 16 * mb) =
-          make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-    if (g == 0) lse[static_cast<size_t>(bh) * T + i] = L;
+          make_float4(acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv);
+    if (g == 0) lse[static_cast<size_t>(bh) * T + i] = (m + lg2(l)) * 0.6931471805599453f;
   }
 }
-
 
 // ---------------------------------------------------------------- backward
 // Query side, one wavefront per 15-query tile (same key blocks as the
