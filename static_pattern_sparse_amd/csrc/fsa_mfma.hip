@@ -48,6 +48,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 constexpr int kTileQ = 15;          // queries per wavefront tile
+constexpr int kTileK = 14;          // key rows per dk/dv tile
 constexpr int kMaxWinBlocks = 3;    // window blocks: W <= 33
 constexpr int kLdsRowBytes = 72;    // one d-row of V^T: 32 keys (64 B) + pad
 
@@ -391,14 +392,43 @@ __device__ __forceinline__ TileLane<D> tile_lane(int lane) {
 
 // Issue the loads of rows row0..row0+15 into the LDS block at `dst`. Rows
 // outside the slab are not read (buffer range check).
-template <int D>
-__device__ __forceinline__ void stage_block(rsrc_t r, const TileLane<D>& tl,
+template <int D, typename R>
+__device__ __forceinline__ void stage_block(R r, const TileLane<D>& tl,
                                             int row0, lds_char* dst) {
   using Tl = Tile<D>;
 #pragma unroll
   for (int ii = 0; ii < Tl::kLoads; ++ii)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, dst + ii * 1024, 16, whole(row0 * Tl::kRowBytes + tl.src[ii]), 0, 0, 0);
+}
+
+// Stage rows r0.. and r1.. (INT_MIN: absent) of tensors A and B into the four
+// blocks A_x A_y B_x B_y of an LDS stage.
+template <int D, typename R>
+__device__ __forceinline__ void stage_two(R ra, R rb, const TileLane<D>& tl, int r0,
+                                          int r1, lds_char* st) {
+  constexpr int kB = Tile<D>::kBlockBytes;
+  if (r0 != INT_MIN) {
+    stage_block<D>(ra, tl, r0, st);
+    stage_block<D>(rb, tl, r0, st + 2 * kB);
+  }
+  if (r1 != INT_MIN) {
+    stage_block<D>(ra, tl, r1, st + kB);
+    stage_block<D>(rb, tl, r1, st + 3 * kB);
+  }
+}
+
+// First row of block hf of pair p: `nwp` pairs of 16-row blocks
+// base0 + step*b (b < nb) come first, then pairs of taps at base1 + sgn*c_t.
+__device__ __forceinline__ int pair_row(int p, int hf, int nwp, int nb, int base0,
+                                        int step, int ntap, int base1, int sgn,
+                                        const Taps& taps) {
+  if (p < nwp) {
+    const int b = 2 * p + hf;
+    return b < nb ? base0 + step * b : INT_MIN;
+  }
+  const int t = 2 * (p - nwp) + hf;
+  return t < ntap ? base1 + sgn * taps.c[t] : INT_MIN;
 }
 
 template <int D>
@@ -478,29 +508,13 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   zero_lds(lds, 2 * kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
 
-  // rows of block hf of pair p (INT_MIN: no block)
-  auto block_row = [&](int p, int hf) -> int {
-    if (p < nwp) {
-      const int b = 2 * p + hf;
-      return b < nwb ? i0 - 16 * b : INT_MIN;
-    }
-    const int t = 2 * (p - nwp) + hf;
-    return t < ntap ? i0 - taps.c[t] : INT_MIN;
-  };
-  auto stage_pair = [&](int p, lds_char* st) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int r0 = block_row(p, hf);
-      if (r0 != INT_MIN) {
-        stage_block<D>(rk, tl, r0, st + hf * Tl::kBlockBytes);
-        stage_block<D>(rv, tl, r0, st + (2 + hf) * Tl::kBlockBytes);
-      }
-    }
-  };
+  // rows of block hf of pair p (INT_MIN: no block): window blocks i0-16b,
+  // then taps i0-c_t
+#define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nwb, i0, -16, ntap, i0, -1, taps)
 
   u32x4 qb[D / 32];
   bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
-  stage_pair(0, lds);
+  stage_two<D>(rk, rv, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
 
   f32x4 acc[D / 16];
 #pragma unroll
@@ -510,7 +524,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   for (int p = 0; p < npair; ++p) {
     lds_char* st = lds + (p & 1) * kStage;
     if (p + 1 < npair) {
-      stage_pair(p + 1, lds + ((p + 1) & 1) * kStage);
+      stage_two<D>(rk, rv, tl, BLOCK_ROW(p + 1, 0), BLOCK_ROW(p + 1, 1), lds + ((p + 1) & 1) * kStage);
       wait_vm<4 * Tl::kLoads>();                      // this pair's loads done
     } else {
       wait_vm<0>();
@@ -524,7 +538,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sv[hf][j] = -INFINITY;
-      const int r0 = block_row(p, hf);
+      const int r0 = BLOCK_ROW(p, hf);
       if (r0 == INT_MIN) continue;
       u32x4 ka[D / 32];
       nat_operand<D>(st + hf * Tl::kBlockBytes, tl, ka);
@@ -609,18 +623,22 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   }
 }
 
+#undef BLOCK_ROW
 // ---------------------------------------------------------------- backward
-// Query side, one wavefront per 15-query tile (same key blocks as the
-// forward). For every attended entry e of query i, with p = exp(s - lse_i):
-//   dP_e = dout_i . value_e,  Delta_i = sum_e p_e dP_e,  dS_e = p_e (dP_e - Delta_i),
-//   dq_i = scale * sum_e dS_e key_e.
-// S^T and dP^T of a block come from two MFMA products (K and V rows as A,
-// the tile's q and dout rows as B). dq^T = K^T dS^T runs over pairs of
-// blocks with K^T staged through LDS, like V^T in the forward. A tap entry's
-// alpha gradient is -f * [dS * scale * q.(K[a+1]-K[a]) + p * dout.(V[a+1]-V[a])]
-// (moving alpha moves the sample point i - alpha*f; Depth-Staggered Fibonacci
-// Spacing, Methodology > Architecture and attention > Implementation); one
-// partial per wavefront goes to `partials`, Delta_i to `delta`.
+// Query side: one wavefront per 15-query tile, the forward's key blocks and
+// pair pipeline (K and V of the next pair in flight). For each attended entry
+// e of query i, with p = exp(s - lse_i) and dP_e = dout_i . value_e:
+//   Delta_i = sum_e p_e dP_e,  dS_e = p_e (dP_e - Delta_i),
+//   dq_i = scale * sum_e dS_e key_e
+//        = scale * (sum_e p_e dP_e key_e - Delta_i sum_e p_e key_e),
+// so one pass accumulates the two products K^T (P o dP) and K^T P (MFMA, K^T
+// read transposed from the same LDS tile) and applies Delta_i at the end.
+// Likewise the alpha gradient of a tap entry, moving the sample point
+// i - alpha*f (Depth-Staggered Fibonacci Spacing, Methodology > Architecture
+// and attention > Implementation),
+//   -f * [dS * scale * q.(K[a+1]-K[a]) + p * dout.(V[a+1]-V[a])]
+// = A - Delta_i * B with A, B accumulated per query. The wavefront writes
+// Delta_i, dq, and one dalpha partial.
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -628,7 +646,11 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     const float* __restrict__ lse, Problem pr, Taps taps, int n_tiles,
     float* __restrict__ dq, float* __restrict__ delta,
     float* __restrict__ partials) {
-  __shared__ __attribute__((aligned(16))) char lds[D * kLdsRowBytes];
+  using Tl = Tile<D>;
+  constexpr int kStage = 4 * Tl::kBlockBytes;          // K_x K_y V_x V_y
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
   const int n = lane & 15, g = lane >> 4;
   const int T = pr.T, W = pr.W;
@@ -636,181 +658,165 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   map_tile(blockIdx.x, pr.B * pr.H, n_tiles, &bh, &tile);
   const int i0 = tile * kTileQ;
   const size_t base = static_cast<size_t>(bh) * T * D;
-  const uint16_t* Q = q + base;
-  const uint16_t* K = k + base;
-  const uint16_t* V = v + base;
-  const uint16_t* G = dout + base;
+  const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
+  const rsrc_t rq = make_rsrc(q + base, slab);
+  const rsrc_t rk = make_rsrc(k + base, slab);
+  const rsrc_t rv = make_rsrc(v + base, slab);
+  const rsrc_t rg = make_rsrc(dout + base, slab);
+  const TileLane<D> tl = tile_lane<D>(lane);
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
-  const int ic = clampi(i, 0, T - 1);
-
-  u32x4 qb[D / 32], gb[D / 32];
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    qb[s] = ld16(Q + static_cast<size_t>(ic) * D + 8 * g + 32 * s);
-    gb[s] = ld16(G + static_cast<size_t>(ic) * D + 8 * g + 32 * s);
-  }
-  const float L = qvalid ? lse[static_cast<size_t>(bh) * T + i] : 0.f;
   const float scale = pr.scale;
+  const float c2 = scale * kLog2e;
+  const float L2 = qvalid ? lse[static_cast<size_t>(bh) * T + i] * kLog2e : 0.f;
+  const LaneMasks lm = lane_masks(n, g);
   const int nwb = (W + kTileQ - 1) / 16 + 1;
   const int last = min(i0 + kTileQ - 1, T - 1);
   int ntap = 0;
   while (ntap < taps.n && taps.c[ntap] <= last) ++ntap;
+  const int nwp = (nwb + 1) / 2;
+  const int npair = nwp + (ntap + 1) / 2;
 
-  // ---- p and dP of every entry, Delta
-  float pw[kMaxWinBlocks][4], gw[kMaxWinBlocks][4];
-  float pt[kNumTaps], gt[kNumTaps], sdf[kNumTaps], gdf[kNumTaps];
-  float dpart = 0.f;
-#pragma unroll
-  for (int b = 0; b < kMaxWinBlocks; ++b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { pw[b][j] = 0.f; gw[b][j] = 0.f; }
-    if (b < nwb) {
-      const f32x4 s = score_block<D>(K, i0 - 16 * b, T, qb, n, g);
-      const f32x4 d = score_block<D>(V, i0 - 16 * b, T, gb, n, g);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rel = 4 * g + j - 16 * b;
-        const bool ok = qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
-        pw[b][j] = ok ? __expf(s[j] * scale - L) : 0.f;
-        gw[b][j] = d[j];
-        dpart += pw[b][j] * d[j];
-      }
-    }
-  }
-  float Dl = xsum4(dpart);
-#pragma unroll
-  for (int t = 0; t < kNumTaps; ++t) {
-    pt[t] = 0.f; gt[t] = 0.f; sdf[t] = 0.f; gdf[t] = 0.f;
-    if (t < ntap) {
-      const int c = taps.c[t];
-      const float wl = taps.w_lo[t], wh = taps.w_hi[t];
-      const f32x4 s = score_block<D>(K, i0 - c, T, qb, n, g);
-      const f32x4 d = score_block<D>(V, i0 - c, T, gb, n, g);
-      float ps = 0.f, pd = 0.f, ds = 0.f, dd = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = 4 * g + j;
-        const float lo = key == n ? 1.f : 0.f, hi = key == n + 1 ? 1.f : 0.f;
-        ps += (wl * lo + wh * hi) * s[j];
-        pd += (wl * lo + wh * hi) * d[j];
-        ds += (hi - lo) * s[j];
-        dd += (hi - lo) * d[j];
-      }
-      ps = xsum4(ps); pd = xsum4(pd); ds = xsum4(ds); dd = xsum4(dd);
-      const bool ok = qvalid && i >= c;
-      pt[t] = ok ? __expf(ps * scale - L) : 0.f;
-      gt[t] = pd;
-      sdf[t] = ds;
-      gdf[t] = dd;
-      Dl += pt[t] * pd;
-    }
-  }
+  zero_lds(lds, 2 * kStage, lane);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
 
-  // ---- dS, dalpha, dq^T = K^T dS^T
-  float dal = 0.f;
-  f32x4 acc[D / 16];
+#define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nwb, i0, -16, ntap, i0, -1, taps)
+
+  u32x4 qb[D / 32], gb[D / 32];
+  bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
+  bload_rows<D>(rg, 16 * g + n * 2 * D, i0, gb);
+  stage_two<D>(rk, rv, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+
+  f32x4 a1[D / 16], a2[D / 16];
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nblk = nwb + ntap;
-  for (int pb = 0; pb < nblk; pb += 2) {
-    float dsv[8];
-    int rows[2];
+  for (int mb = 0; mb < D / 16; ++mb) {
+    a1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a2[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float dwin = 0.f, dtap = 0.f, al_a = 0.f, al_b = 0.f;
+
+  for (int p = 0; p < npair; ++p) {
+    lds_char* st = lds + (p & 1) * kStage;
+    if (p + 1 < npair) {
+      stage_two<D>(rk, rv, tl, BLOCK_ROW(p + 1, 0), BLOCK_ROW(p + 1, 1), lds + ((p + 1) & 1) * kStage);
+      wait_vm<4 * Tl::kLoads>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_wave_barrier();
+    const bool win = p < nwp;
+    float w1[8], w2[8];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int blk = pb + hf;
-      if (blk >= nblk) {
-        rows[hf] = INT_MIN;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dsv[4 * hf + j] = 0.f;
-      } else if (blk < nwb) {
-        rows[hf] = i0 - 16 * blk;
+      for (int j = 0; j < 4; ++j) { w1[4 * hf + j] = 0.f; w2[4 * hf + j] = 0.f; }
+      const int r0 = BLOCK_ROW(p, hf);
+      if (r0 == INT_MIN) continue;
+      u32x4 ka[D / 32], va[D / 32];
+      nat_operand<D>(st + hf * Tl::kBlockBytes, tl, ka);
+      nat_operand<D>(st + (2 + hf) * Tl::kBlockBytes, tl, va);
+      const f32x4 s = mfma_rows<D>(ka, qb);
+      const f32x4 d = mfma_rows<D>(va, gb);
+      if (win) {
+        const int b = 2 * p + hf;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float p = pw[0][j], d = gw[0][j];
-#pragma unroll
-          for (int b = 1; b < kMaxWinBlocks; ++b) {
-            p = blk == b ? pw[b][j] : p;
-            d = blk == b ? gw[b][j] : d;
-          }
-          dsv[4 * hf + j] = p * (d - Dl);
+          const int rel = 4 * g + j - 16 * b;
+          const bool ok = qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
+          const float pe = ok ? ex2(s[j] * c2 - L2) : 0.f;
+          w1[4 * hf + j] = pe * d[j];
+          w2[4 * hf + j] = pe;
+          dwin += pe * d[j];
         }
       } else {
-        const int t = blk - nwb;
-        float p = pt[0], d = gt[0], sd = sdf[0], gd = gdf[0];
-        float wl = taps.w_lo[0], wh = taps.w_hi[0], nf = taps.neg_f[0];
-        int c = taps.c[0];
-#pragma unroll
-        for (int u = 1; u < kNumTaps; ++u) {
-          if (t == u) {
-            p = pt[u]; d = gt[u]; sd = sdf[u]; gd = gdf[u];
-            wl = taps.w_lo[u]; wh = taps.w_hi[u]; nf = taps.neg_f[u]; c = taps.c[u];
-          }
-        }
-        rows[hf] = i0 - c;
-        const float ds = p * (d - Dl);
-        if (g == 0) dal += nf * (ds * scale * sd + p * gd);
+        const int t = 2 * (p - nwp) + hf;
+        const float wl = taps.w_lo[t], wh = taps.w_hi[t];
+        float slo = 0.f, shi = 0.f, dlo = 0.f, dhi = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int key = 4 * g + j;
-          dsv[4 * hf + j] = key == n ? ds * wl : (key == n + 1 ? ds * wh : 0.f);
+          slo = fmaf(lm.mlo[j], s[j], slo);
+          shi = fmaf(lm.mhi[j], s[j], shi);
+          dlo = fmaf(lm.mlo[j], d[j], dlo);
+          dhi = fmaf(lm.mhi[j], d[j], dhi);
+        }
+        const float ps = rsum4(wl * slo + wh * shi);
+        const float pd = rsum4(wl * dlo + wh * dhi);
+        const float sdf = rsum4(shi - slo);
+        const float gdf = rsum4(dhi - dlo);
+        const bool ok = qvalid && i >= taps.c[t];
+        const float pe = ok ? ex2(ps * c2 - L2) : 0.f;
+        dtap += pe * pd;
+        const float nf = taps.neg_f[t];
+        al_a += nf * pe * (pd * scale * sdf + gdf);
+        al_b += nf * pe * scale * sdf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float wt = wl * lm.mlo[j] + wh * lm.mhi[j];
+          w1[4 * hf + j] = pe * pd * wt;
+          w2[4 * hf + j] = pe * wt;
         }
       }
     }
-    __syncthreads();
-    stage_t<D>(K, rows[0], T, lds, 0, lane);
-    stage_t<D>(K, rows[1], T, lds, 1, lane);
-    __syncthreads();
-    u32x4 bhi, blo;
-    split_hi_lo(dsv, &bhi, &blo);
+    u32x4 h1, l1, h2, l2;
+    split8(w1, &h1, &l1);
+    split8(w2, &h2, &l2);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 a = t_operand(lds, mb, n, g);
-      acc[mb] = mfma(a, bhi, acc[mb]);
-      acc[mb] = mfma(a, blo, acc[mb]);
+      const u32x4 a = tr_operand<D>(st, st + Tl::kBlockBytes, tl, mb);
+      a1[mb] = mfma(a, h1, a1[mb]);
+      a1[mb] = mfma(a, l1, a1[mb]);
+      a2[mb] = mfma(a, h2, a2[mb]);
+      a2[mb] = mfma(a, l2, a2[mb]);
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
   }
 
+  const float Dl = rsum4(dwin) + dtap;
   if (qvalid) {
     float* o = dq + base + static_cast<size_t>(i) * D + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb)
       *reinterpret_cast<float4*>(o + 16 * mb) =
-          make_float4(acc[mb][0] * scale, acc[mb][1] * scale,
-                      acc[mb][2] * scale, acc[mb][3] * scale);
+          make_float4(scale * (a1[mb][0] - Dl * a2[mb][0]), scale * (a1[mb][1] - Dl * a2[mb][1]),
+                      scale * (a1[mb][2] - Dl * a2[mb][2]), scale * (a1[mb][3] - Dl * a2[mb][3]));
     if (g == 0) delta[static_cast<size_t>(bh) * T + i] = Dl;
   }
+  float dal = (g == 0) ? al_a - Dl * al_b : 0.f;       // al_* are replicated over g
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) dal += __shfl_xor(dal, off);
   if (lane == 0) partials[blockIdx.x] = dal;
 }
 
-// Key side, one wavefront per tile of kTileK = 14 key rows j0..j0+13, handled
+#undef BLOCK_ROW
+// Key side: one wavefront per tile of kTileK = 14 key rows j0..j0+13, handled
 // as the 16-row block rowb = j0-1 .. j0+14 (the two end rows are halos whose
 // sums are discarded). Row r of the block collects
 //   window: dk_r += scale dS_ir q_i, dv_r += p_ir dout_i for i = r..r+W-1;
 //   tap:    the same with weight 1-t from query r + c and weight t from query
 //           r + c - 1 (r is then the upper interpolation row).
-// For a tap, the 15 queries ib = j0+c-1 .. ib+14 use block rows n' and n'+1,
-// exactly the forward's tile/block geometry with the roles swapped. Their
-// scores are recomputed with S = Q_span K_blk^T (query rows as A, the block's
-// key rows as B held in registers), so lane (g, m) holds query 4g+j against
-// key m: a tap score needs lanes m and m+1 of the same 16-lane row. The
-// weighted dS (and p) blocks are then exactly the B operand of
-// dk^T += Q_span^T (W o dS), dv^T += dout_span^T (W o P), over pairs of blocks,
-// with Q^T and dout^T staged through LDS.
-constexpr int kTileK = 14;
-
+// The query rows involved come in 16-row query blocks: window blocks
+// rowb + 16b, and for a tap the 15 queries ib = j0+c-1 .. ib+14, which use
+// block rows n' and n'+1 (the forward's geometry with the roles swapped).
+// Query and dout blocks of a pair are staged in LDS (next pair in flight);
+// scores are recomputed as S = Q_blk K^T (query rows natural from LDS as A,
+// the tile's key rows as B in registers), so lane (g, m) holds query 4g+j
+// against key m and a tap score needs lanes m and m+1 of one 16-lane row.
+// dk^T += Q_blk^T (W o dS) and dv^T += dout_blk^T (W o P) read Q^T and dout^T
+// transposed from the same LDS tiles.
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, Problem pr,
     Taps taps, int n_tiles, float* __restrict__ dk, float* __restrict__ dv) {
-  __shared__ __attribute__((aligned(16))) char ldq[D * kLdsRowBytes];
-  __shared__ __attribute__((aligned(16))) char ldg[D * kLdsRowBytes];
+  using Tl = Tile<D>;
+  constexpr int kStage = 4 * Tl::kBlockBytes;          // Q_x Q_y G_x G_y
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
-  const int n = lane & 15, g = lane >> 4;          // n: key row m of the block
+  const int n = lane & 15, g = lane >> 4;              // n: key row m of the block
   const int T = pr.T, W = pr.W;
   int bh, tile;
   map_tile(blockIdx.x, pr.B * pr.H, n_tiles, &bh, &tile);
@@ -818,24 +824,29 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const int rowb = j0 - 1;
   const size_t base = static_cast<size_t>(bh) * T * D;
   const size_t rbase = static_cast<size_t>(bh) * T;
-  const uint16_t* Q = q + base;
-  const uint16_t* K = k + base;
-  const uint16_t* V = v + base;
-  const uint16_t* G = dout + base;
+  const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
+  const rsrc_t rq = make_rsrc(q + base, slab);
+  const rsrc_t rk = make_rsrc(k + base, slab);
+  const rsrc_t rv = make_rsrc(v + base, slab);
+  const rsrc_t rg = make_rsrc(dout + base, slab);
+  const TileLane<D> tl = tile_lane<D>(lane);
   const float scale = pr.scale;
+  const float c2 = scale * kLog2e;
+  const int nqb = (W + kTileK + 15) / 16;              // window query blocks
+  int ntap = 0;                                         // taps with a query < T
+  while (ntap < taps.n && j0 + taps.c[ntap] - 1 <= T - 1) ++ntap;
+  const int nwp = (nqb + 1) / 2;
+  const int npair = nwp + (ntap + 1) / 2;
+
+  zero_lds(lds, 2 * kStage, lane);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+
+#define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nqb, rowb, 16, ntap, j0 - 1, 1, taps)
 
   u32x4 kb[D / 32], vb[D / 32];
-  {
-    const int r = clampi(rowb + n, 0, T - 1);
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      kb[s] = ld16(K + static_cast<size_t>(r) * D + 8 * g + 32 * s);
-      vb[s] = ld16(V + static_cast<size_t>(r) * D + 8 * g + 32 * s);
-    }
-  }
-  const int nqb = (W + kTileK + 15) / 16;          // window query blocks
-  int ntap = 0;                                     // taps with a query < T
-  while (ntap < taps.n && j0 + taps.c[ntap] - 1 <= T - 1) ++ntap;
+  bload_rows<D>(rk, 16 * g + n * 2 * D, rowb, kb);
+  bload_rows<D>(rv, 16 * g + n * 2 * D, rowb, vb);
+  stage_two<D>(rq, rg, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
 
   f32x4 ak[D / 16], av[D / 16];
 #pragma unroll
@@ -843,49 +854,46 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     ak[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     av[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int nblk = nqb + ntap;
-  for (int pb = 0; pb < nblk; pb += 2) {
+  const int r = rowb + n;                               // this lane's key row
+  const int jj = n - 4 * g;                             // reg holding query m
+
+  for (int p = 0; p < npair; ++p) {
+    lds_char* st = lds + (p & 1) * kStage;
+    if (p + 1 < npair) {
+      stage_two<D>(rq, rg, tl, BLOCK_ROW(p + 1, 0), BLOCK_ROW(p + 1, 1), lds + ((p + 1) & 1) * kStage);
+      wait_vm<4 * Tl::kLoads>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_wave_barrier();
+    const bool win = p < nwp;
     float pv[8], dsv[8];
-    int rows[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int blk = pb + hf;
-      if (blk >= nblk) {
-        rows[hf] = INT_MIN;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { pv[4 * hf + j] = 0.f; dsv[4 * hf + j] = 0.f; }
-      } else if (blk < nqb) {
-        // window: queries ib + 4g + j against key rowb + n
-        const int ib = rowb + 16 * blk;
-        rows[hf] = ib;
-        const f32x4 s = score_block<D>(Q, ib, T, kb, n, g);
-        const f32x4 d = score_block<D>(G, ib, T, vb, n, g);
-        const int r = rowb + n;
+      for (int j = 0; j < 4; ++j) { pv[4 * hf + j] = 0.f; dsv[4 * hf + j] = 0.f; }
+      const int ib = BLOCK_ROW(p, hf);
+      if (ib == INT_MIN) continue;
+      u32x4 qa[D / 32], ga[D / 32];
+      nat_operand<D>(st + hf * Tl::kBlockBytes, tl, qa);
+      nat_operand<D>(st + (2 + hf) * Tl::kBlockBytes, tl, ga);
+      const f32x4 s = mfma_rows<D>(qa, kb);
+      const f32x4 d = mfma_rows<D>(ga, vb);
+      if (win) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int iq = ib + 4 * g + j;
           const int rel = iq - r;
           const bool ok = iq < T && r >= 0 && rel >= 0 && rel < W;
           const int ii = clampi(iq, 0, T - 1);
-          const float p = ok ? __expf(s[j] * scale - lse[rbase + ii]) : 0.f;
-          pv[4 * hf + j] = p;
-          dsv[4 * hf + j] = p * (d[j] - (ok ? delta[rbase + ii] : 0.f));
+          const float pe = ok ? ex2(s[j] * c2 - lse[rbase + ii] * kLog2e) : 0.f;
+          pv[4 * hf + j] = pe;
+          dsv[4 * hf + j] = ok ? pe * (d[j] - delta[rbase + ii]) : 0.f;
         }
       } else {
-        const int t = blk - nqb;
-        float wl = taps.w_lo[0], wh = taps.w_hi[0];
-        int c = taps.c[0];
-#pragma unroll
-        for (int u = 1; u < kNumTaps; ++u) {
-          if (t == u) { wl = taps.w_lo[u]; wh = taps.w_hi[u]; c = taps.c[u]; }
-        }
-        const int ib = j0 + c - 1;                 // query of span row 0
-        rows[hf] = ib;
-        const f32x4 s = score_block<D>(Q, ib, T, kb, n, g);
-        const f32x4 d = score_block<D>(G, ib, T, vb, n, g);
-        // query m (this lane's column) reads key rows m (lo) and m + 1 (hi)
+        const int t = 2 * (p - nwp) + hf;
+        const float wl = taps.w_lo[t], wh = taps.w_hi[t];
         float s_lo = 0.f, s_hi = 0.f, d_lo = 0.f, d_hi = 0.f;
-        const int jj = n - 4 * g;                  // reg holding query m here
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float su = __shfl_down(s[j], 1, 16);
@@ -893,55 +901,50 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
           if (jj == j) { s_lo = s[j]; s_hi = su; d_lo = d[j]; d_hi = du; }
         }
         const int iq = ib + n;
-        const bool ok = jj >= 0 && jj < 4 && n < kTileQ && iq < T && iq >= c;
+        const bool ok = jj >= 0 && jj < 4 && n < kTileQ && iq < T && iq >= taps.c[t];
         const int ii = clampi(iq, 0, T - 1);
-        const float p = ok ? __expf((wl * s_lo + wh * s_hi) * scale - lse[rbase + ii]) : 0.f;
-        const float ds = ok ? p * (wl * d_lo + wh * d_hi - delta[rbase + ii]) : 0.f;
-        const float p_up = __shfl_up(p, 1, 16);     // query m-1's values
+        const float pe = ok ? ex2((wl * s_lo + wh * s_hi) * c2 - lse[rbase + ii] * kLog2e) : 0.f;
+        const float ds = ok ? pe * (wl * d_lo + wh * d_hi - delta[rbase + ii]) : 0.f;
+        const float p_up = __shfl_up(pe, 1, 16);        // query m-1's values
         const float ds_up = __shfl_up(ds, 1, 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int qn = 4 * g + j;                 // query of reg j
-          pv[4 * hf + j] = n == qn ? wl * p : (n == qn + 1 ? wh * p_up : 0.f);
+          const int qn = 4 * g + j;                      // query of reg j
+          pv[4 * hf + j] = n == qn ? wl * pe : (n == qn + 1 ? wh * p_up : 0.f);
           dsv[4 * hf + j] = n == qn ? wl * ds : (n == qn + 1 ? wh * ds_up : 0.f);
         }
       }
     }
-    __syncthreads();
-    stage_t<D>(Q, rows[0], T, ldq, 0, lane);
-    stage_t<D>(Q, rows[1], T, ldq, 1, lane);
-    stage_t<D>(G, rows[0], T, ldg, 0, lane);
-    stage_t<D>(G, rows[1], T, ldg, 1, lane);
-    __syncthreads();
     u32x4 phi, plo, shi, slo;
-    split_hi_lo(pv, &phi, &plo);
-    split_hi_lo(dsv, &shi, &slo);
+    split8(pv, &phi, &plo);
+    split8(dsv, &shi, &slo);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 aq = t_operand(ldq, mb, n, g);
+      const u32x4 aq = tr_operand<D>(st, st + Tl::kBlockBytes, tl, mb);
       ak[mb] = mfma(aq, shi, ak[mb]);
       ak[mb] = mfma(aq, slo, ak[mb]);
-      const u32x4 ag = t_operand(ldg, mb, n, g);
+      const u32x4 ag = tr_operand<D>(st + 2 * Tl::kBlockBytes, st + 3 * Tl::kBlockBytes, tl, mb);
       av[mb] = mfma(ag, phi, av[mb]);
       av[mb] = mfma(ag, plo, av[mb]);
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
   }
 
-  const int r = rowb + n;
   if (n >= 1 && n <= kTileK && r < T) {
-    float* ok_ = dk + base + static_cast<size_t>(r) * D + 4 * g;
-    float* ov = dv + base + static_cast<size_t>(r) * D + 4 * g;
+    float* okp = dk + base + static_cast<size_t>(r) * D + 4 * g;
+    float* ovp = dv + base + static_cast<size_t>(r) * D + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      *reinterpret_cast<float4*>(ok_ + 16 * mb) =
-          make_float4(ak[mb][0] * scale, ak[mb][1] * scale, ak[mb][2] * scale,
-                      ak[mb][3] * scale);
-      *reinterpret_cast<float4*>(ov + 16 * mb) =
+      *reinterpret_cast<float4*>(okp + 16 * mb) =
+          make_float4(ak[mb][0] * scale, ak[mb][1] * scale, ak[mb][2] * scale, ak[mb][3] * scale);
+      *reinterpret_cast<float4*>(ovp + 16 * mb) =
           make_float4(av[mb][0], av[mb][1], av[mb][2], av[mb][3]);
     }
   }
 }
 
+#undef BLOCK_ROW
 }  // namespace
 
 bool mfma_supported(const Problem& pr, int dtype) {
