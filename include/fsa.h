@@ -139,13 +139,13 @@ int fsa_backward(const void* q, const void* k, const void* v,
                  size_t workspace_bytes, void* stream);
 
 /*
- * Split-phase backward: the same three stages fsa_backward runs, for callers
+ * Split-phase backward: the same two stages fsa_backward runs, for callers
  * that interleave other work between them or time them separately. They must
  * run in this order on one stream, with the same arguments and workspace:
- *   fsa_backward_dq      writes dq, and the per-row softmax terms and per-tile
- *                        dalpha partials into the workspace;
- *   fsa_backward_dkdv    writes dk and dv (reads the per-row terms);
- *   fsa_backward_dalpha  writes dalpha[0] (reduces the partials in a fixed order).
+ *   fsa_backward_dq    writes dq, and the per-row softmax terms and per-tile
+ *                      dalpha partials into the workspace;
+ *   fsa_backward_dkdv  writes dk and dv (reads the per-row terms) and
+ *                      dalpha[0] (sums the partials in a fixed order).
  * Arguments, layouts and errors are those of fsa_backward.
  */
 int fsa_backward_dq(const void* q, const void* k, const void* v,
@@ -155,11 +155,8 @@ int fsa_backward_dq(const void* q, const void* k, const void* v,
 int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                       const void* dout, const float* lse, int dtype, int B,
                       int H, int T, int D, float alpha, int window, float* dk,
-                      float* dv, void* workspace, size_t workspace_bytes,
-                      void* stream);
-int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float alpha,
-                        int window, float* dalpha, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                      float* dv, float* dalpha, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* fsa_status_string -- static text for a status code. */
 const char* fsa_status_string(int status);

@@ -155,13 +155,17 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
                            const void* dout, const float* lse,
-                           const float* delta, int dtype, const Problem& pr,
-                           const Taps& taps, float* dk, float* dv,
-                           hipStream_t s) {
+                           const float* delta, const float* partials,
+                           int dtype, const Problem& pr, const Taps& taps,
+                           float* dk, float* dv, float* dalpha, hipStream_t s) {
+  const size_t np = bwd_partials_used(pr, dtype);
   if (mfma_supported(pr, dtype))
-    return launch_bwd_dkdv_mfma(q, k, v, dout, lse, delta, pr, taps, dk, dv, s);
-  return launch_bwd_dkdv_vec(q, k, v, dout, lse, delta, dtype, pr, taps, dk,
-                             dv, s);
+    return launch_bwd_dkdv_mfma(q, k, v, dout, lse, delta, partials, np, pr,
+                                taps, dk, dv, dalpha, s);
+  hipError_t e = launch_bwd_dkdv_vec(q, k, v, dout, lse, delta, dtype, pr, taps,
+                                     dk, dv, s);
+  if (e != hipSuccess) return e;
+  return launch_dalpha_reduce(partials, np, dalpha, s);
 }
 
 size_t bwd_partials_used(const Problem& pr, int dtype) {
@@ -259,36 +263,18 @@ int fsa_backward_dq(const void* q, const void* k, const void* v,
 int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                       const void* dout, const float* lse, int dtype, int B,
                       int H, int T, int D, float alpha, int window, float* dk,
-                      float* dv, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      float* dv, float* dalpha, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   BwdArgs a;
   int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
                      workspace, workspace_bytes, &a);
-  if (st != FSA_OK || a.empty) return st;
-  if (!dk || !dv || !aligned16(dk) || !aligned16(dv)) return FSA_ERR_INVALID_ARG;
-  return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, dtype, a.pr,
-                                    a.taps, dk, dv,
-                                    static_cast<hipStream_t>(stream)));
-}
-
-int fsa_backward_dalpha(int dtype, int B, int H, int T, int D, float alpha,
-                        int window, float* dalpha, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  int st = check_shape(dtype, B, H, T, D, alpha, window);
   if (st != FSA_OK) return st;
   if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (static_cast<long long>(B) * H * T == 0)
-    return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
-  const BwdWorkspace ws = bwd_workspace_layout(B, H, T, D, dtype);
-  if (workspace == nullptr || workspace_bytes < ws.total ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return FSA_ERR_WORKSPACE;
-  const Problem pr = make_problem(B, H, T, D, window);
-  const float* partials = reinterpret_cast<const float*>(
-      static_cast<const char*>(workspace) + ws.partial_off);
-  return hip_status(launch_dalpha_reduce(partials, bwd_partials_used(pr, dtype),
-                                         dalpha, s));
+  if (a.empty) return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
+  if (!dk || !dv || !aligned16(dk) || !aligned16(dv)) return FSA_ERR_INVALID_ARG;
+  return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, a.partials,
+                                    dtype, a.pr, a.taps, dk, dv, dalpha, s));
 }
 
 int fsa_backward(const void* q, const void* k, const void* v,
@@ -309,11 +295,8 @@ int fsa_backward(const void* q, const void* k, const void* v,
   st = hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
                                 a.delta, a.partials, s));
   if (st != FSA_OK) return st;
-  st = hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, dtype, a.pr,
-                                  a.taps, dk, dv, s));
-  if (st != FSA_OK) return st;
-  return hip_status(launch_dalpha_reduce(
-      a.partials, bwd_partials_used(a.pr, dtype), dalpha, s));
+  return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, a.partials,
+                                    dtype, a.pr, a.taps, dk, dv, dalpha, s));
 }
 
 const char* fsa_status_string(int status) {

@@ -45,11 +45,12 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, int dtype,
                          const Problem& pr, const Taps& taps, float* dq,
                          float* delta, float* partials, hipStream_t s);
+// dk, dv, and dalpha[0] = fixed-order sum of the dq stage's partials
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
                            const void* dout, const float* lse,
-                           const float* delta, int dtype, const Problem& pr,
-                           const Taps& taps, float* dk, float* dv,
-                           hipStream_t s);
+                           const float* delta, const float* partials,
+                           int dtype, const Problem& pr, const Taps& taps,
+                           float* dk, float* dv, float* dalpha, hipStream_t s);
 // number of dalpha partials the dq stage writes for this problem
 size_t bwd_partials_used(const Problem& pr, int dtype);
 hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
@@ -81,9 +82,10 @@ hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               float* delta, float* partials, hipStream_t s);
 hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse,
-                                const float* delta, const Problem& pr,
+                                const float* delta, const float* partials,
+                                size_t n_partials, const Problem& pr,
                                 const Taps& taps, float* dk, float* dv,
-                                hipStream_t s);
+                                float* dalpha, hipStream_t s);
 size_t bwd_partials_used_mfma(const Problem& pr);
 
 }  // namespace fsa

@@ -808,8 +808,10 @@ template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, Problem pr,
-    Taps taps, int n_tiles, float* __restrict__ dk, float* __restrict__ dv) {
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ partials, int n_partials, Problem pr, Taps taps,
+    int n_tiles, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dalpha) {
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // Q_x Q_y G_x G_y
   constexpr float kLog2e = 1.4426950408889634f;
@@ -832,6 +834,16 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const TileLane<D> tl = tile_lane<D>(lane);
   const float scale = pr.scale;
   const float c2 = scale * kLog2e;
+  // The dq stage has finished (same stream): workgroup 0 also sums its
+  // per-tile dalpha partials, in fp64 and a fixed order (lane-strided sums,
+  // then a butterfly).
+  if (blockIdx.x == 0) {
+    double acc = 0.0;
+    for (int x = lane; x < n_partials; x += 64) acc += partials[x];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) dalpha[0] = static_cast<float>(acc);
+  }
   const int nqb = (W + kTileK + 15) / 16;              // window query blocks
   int ntap = 0;                                         // taps with a query < T
   while (ntap < taps.n && j0 + taps.c[ntap] - 1 <= T - 1) ++ntap;
@@ -999,9 +1011,10 @@ hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
 
 hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse,
-                                const float* delta, const Problem& pr,
+                                const float* delta, const float* partials,
+                                size_t n_partials, const Problem& pr,
                                 const Taps& taps, float* dk, float* dv,
-                                hipStream_t s) {
+                                float* dalpha, hipStream_t s) {
   const int n_tiles = (pr.T + kTileK - 1) / kTileK;
   const dim3 grid(n_tiles * pr.B * pr.H);
   const auto* qq = static_cast<const uint16_t*>(q);
@@ -1010,10 +1023,12 @@ hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
   const auto* gg = static_cast<const uint16_t*>(dout);
   if (pr.D == 64)
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, delta, pr, taps, n_tiles, dk, dv);
+                       gg, lse, delta, partials, static_cast<int>(n_partials), pr,
+                       taps, n_tiles, dk, dv, dalpha);
   else
     hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, delta, pr, taps, n_tiles, dk, dv);
+                       gg, lse, delta, partials, static_cast<int>(n_partials), pr,
+                       taps, n_tiles, dk, dv, dalpha);
   return hipGetLastError();
 }
 

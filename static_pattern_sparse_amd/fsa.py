@@ -31,8 +31,7 @@ NUM_TAPS = 15
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsa.so")
 EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_forward",
            "fsa_backward_workspace_size", "fsa_backward", "fsa_backward_dq",
-           "fsa_backward_dkdv", "fsa_backward_dalpha", "fsa_status_string",
-           "fsa_last_hip_error")
+           "fsa_backward_dkdv", "fsa_status_string", "fsa_last_hip_error")
 
 _lib = None
 
@@ -73,11 +72,8 @@ def lib():
                                   f32, i32, vp, vp, ctypes.c_size_t, vp]
     L.fsa_backward_dq.restype = i32
     L.fsa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                    f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+                                    f32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.fsa_backward_dkdv.restype = i32
-    L.fsa_backward_dalpha.argtypes = [i32, i32, i32, i32, i32, f32, i32, vp, vp,
-                                      ctypes.c_size_t, vp]
-    L.fsa_backward_dalpha.restype = i32
     L.fsa_status_string.argtypes = [i32]
     L.fsa_status_string.restype = ctypes.c_char_p
     L.fsa_last_hip_error.argtypes = []
@@ -206,23 +202,14 @@ def fsa_backward_dq(q, k, v, dout, lse, alpha, window, dq, workspace,
     _check("fsa_backward_dq", st)
 
 
-def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, workspace,
-                      stream=None):
-    """Stage 2 of the backward pass: dk and dv."""
+def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, dalpha,
+                      workspace, stream=None):
+    """Stage 2 of the backward pass: dk, dv, and dalpha[0] from the stage-1
+    partials."""
     B, H, T, D = _shape(q)
     st = lib().fsa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                  _ptr(lse), _dtype_code(q), B, H, T, D,
                                  float(alpha), int(window), _ptr(dk), _ptr(dv),
-                                 _ptr(workspace), _ws_bytes(workspace),
-                                 _stream(stream))
+                                 _ptr(dalpha), _ptr(workspace),
+                                 _ws_bytes(workspace), _stream(stream))
     _check("fsa_backward_dkdv", st)
-
-
-def fsa_backward_dalpha(q, alpha, window, dalpha, workspace, stream=None):
-    """Stage 3 of the backward pass: dalpha[0] from the stage-1 partials."""
-    B, H, T, D = _shape(q)
-    st = lib().fsa_backward_dalpha(_dtype_code(q), B, H, T, D, float(alpha),
-                                   int(window), _ptr(dalpha),
-                                   _ptr(workspace), _ws_bytes(workspace),
-                                   _stream(stream))
-    _check("fsa_backward_dalpha", st)

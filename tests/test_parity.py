@@ -162,8 +162,7 @@ def test_split_phase_backward_matches_fused():
     dq, dk, dv = (torch.full_like(ref[0], float("nan")) for _ in range(3))
     da = torch.full((1,), float("nan"), device="cuda")
     F.fsa_backward_dq(q, k, v, g, lse, alpha, W, dq, ws)
-    F.fsa_backward_dkdv(q, k, v, g, lse, alpha, W, dk, dv, ws)
-    F.fsa_backward_dalpha(q, alpha, W, da, ws)
+    F.fsa_backward_dkdv(q, k, v, g, lse, alpha, W, dk, dv, da, ws)
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv, da), ref):
         assert torch.equal(a, b)
