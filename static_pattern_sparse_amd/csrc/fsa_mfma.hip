@@ -469,8 +469,11 @@ __device__ __forceinline__ void wait_vm() {
 
 // ---------------------------------------------------------------- forward
 // One wavefront per 15-query tile. Key blocks are taken in pairs (window pairs
-// first, then tap pairs); K and V of the next pair are in flight while the
-// current pair is processed. Softmax is online over the pairs: running max m
+// first, then tap pairs); K and V of a pair are staged in the wavefront's LDS
+// region (8 KB at D = 64), then consumed. One stage per wavefront keeps the
+// LDS footprint small, so that many wavefronts per CU hide the load latency
+// (a two-stage ring with the next pair in flight measured slower: it halves
+// the resident wavefronts). Softmax is online over the pairs: running max m
 // and sum l (log2 units), the partial output rescaled when m grows.
 template <int D>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;         // K_x K_y V_x V_y
   constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) char smem[kStage];
   lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
   const int n = lane & 15, g = lane >> 4;
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   const int nwp = (nwb + 1) / 2;
   const int npair = nwp + (ntap + 1) / 2;
 
-  zero_lds(lds, 2 * kStage, lane);
+  zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
 
   // rows of block hf of pair p (INT_MIN: no block): window blocks i0-16b,
@@ -522,13 +525,9 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   float m = -INFINITY, l = 0.f;
 
   for (int p = 0; p < npair; ++p) {
-    lds_char* st = lds + (p & 1) * kStage;
-    if (p + 1 < npair) {
-      stage_two<D>(rk, rv, tl, BLOCK_ROW(p + 1, 0), BLOCK_ROW(p + 1, 1), lds + ((p + 1) & 1) * kStage);
-      wait_vm<4 * Tl::kLoads>();                      // this pair's loads done
-    } else {
-      wait_vm<0>();
-    }
+    lds_char* st = lds;
+    if (p > 0) stage_two<D>(rk, rv, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+    wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     // ---- scores of the pair
     float sv[2][4];
@@ -626,7 +625,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
 #undef BLOCK_ROW
 // ---------------------------------------------------------------- backward
 // Query side: one wavefront per 15-query tile, the forward's key blocks and
-// pair pipeline (K and V of the next pair in flight). For each attended entry
+// pair loop (K and V of a pair staged in LDS). For each attended entry
 // e of query i, with p = exp(s - lse_i) and dP_e = dout_i . value_e:
 //   Delta_i = sum_e p_e dP_e,  dS_e = p_e (dP_e - Delta_i),
 //   dq_i = scale * sum_e dS_e key_e
@@ -649,7 +648,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // K_x K_y V_x V_y
   constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) char smem[kStage];
   lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
   const int n = lane & 15, g = lane >> 4;
@@ -677,7 +676,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const int nwp = (nwb + 1) / 2;
   const int npair = nwp + (ntap + 1) / 2;
 
-  zero_lds(lds, 2 * kStage, lane);
+  zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);
 
 #define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nwb, i0, -16, ntap, i0, -1, taps)
@@ -696,13 +695,9 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   float dwin = 0.f, dtap = 0.f, al_a = 0.f, al_b = 0.f;
 
   for (int p = 0; p < npair; ++p) {
-    lds_char* st = lds + (p & 1) * kStage;
-    if (p + 1 < npair) {
-      stage_two<D>(rk, rv, tl, BLOCK_ROW(p + 1, 0), BLOCK_ROW(p + 1, 1), lds + ((p + 1) & 1) * kStage);
-      wait_vm<4 * Tl::kLoads>();
-    } else {
-      wait_vm<0>();
-    }
+    lds_char* st = lds;
+    if (p > 0) stage_two<D>(rk, rv, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+    wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     const bool win = p < nwp;
     float w1[8], w2[8];
@@ -798,14 +793,14 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 // The query rows involved come in 16-row query blocks: window blocks
 // rowb + 16b, and for a tap the 15 queries ib = j0+c-1 .. ib+14, which use
 // block rows n' and n'+1 (the forward's geometry with the roles swapped).
-// Query and dout blocks of a pair are staged in LDS (next pair in flight);
+// Query and dout blocks of a pair are staged in LDS;
 // scores are recomputed as S = Q_blk K^T (query rows natural from LDS as A,
 // the tile's key rows as B in registers), so lane (g, m) holds query 4g+j
 // against key m and a tap score needs lanes m and m+1 of one 16-lane row.
 // dk^T += Q_blk^T (W o dS) and dv^T += dout_blk^T (W o P) read Q^T and dout^T
 // transposed from the same LDS tiles.
 template <int D>
-__global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -815,7 +810,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // Q_x Q_y G_x G_y
   constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) char smem[kStage];
   lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
   const int n = lane & 15, g = lane >> 4;              // n: key row m of the block
@@ -850,7 +845,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const int nwp = (nqb + 1) / 2;
   const int npair = nwp + (ntap + 1) / 2;
 
-  zero_lds(lds, 2 * kStage, lane);
+  zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);
 
 #define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nqb, rowb, 16, ntap, j0 - 1, 1, taps)
@@ -870,13 +865,9 @@ __global__ __launch_bounds__(64) void bwd_dkdv_mfma_kernel(
   const int jj = n - 4 * g;                             // reg holding query m
 
   for (int p = 0; p < npair; ++p) {
-    lds_char* st = lds + (p & 1) * kStage;
-    if (p + 1 < npair) {
-      stage_two<D>(rq, rg, tl, BLOCK_ROW(p + 1, 0), BLOCK_ROW(p + 1, 1), lds + ((p + 1) & 1) * kStage);
-      wait_vm<4 * Tl::kLoads>();
-    } else {
-      wait_vm<0>();
-    }
+    lds_char* st = lds;
+    if (p > 0) stage_two<D>(rq, rg, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+    wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     const bool win = p < nwp;
     float pv[8], dsv[8];
