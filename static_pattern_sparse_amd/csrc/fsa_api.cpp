@@ -128,7 +128,8 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
   // tiling used by the backward pass
   w.n_partials = static_cast<size_t>(B) * H * ((static_cast<size_t>(T) + 7) / 8);
   w.delta_off = 0;
-  w.partial_off = align256(rows * sizeof(float));
+  // per row: (lse * log2(e), Delta) as two floats
+  w.partial_off = align256(rows * 2 * sizeof(float));
   w.total = align256(w.partial_off + w.n_partials * sizeof(float));
   return w;
 }

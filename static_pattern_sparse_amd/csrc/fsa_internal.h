@@ -28,7 +28,8 @@ struct Problem {
 
 // Workspace layout of the backward pass (offsets in bytes, 256-aligned).
 struct BwdWorkspace {
-  size_t delta_off;     // float[B*H*T]: Delta_i = sum_e p_ie dP_ie
+  size_t delta_off;     // per row i: Delta_i = sum_e p_ie dP_ie (and, for the
+                        // tile kernels, float2 {lse_i * log2(e), Delta_i})
   size_t partial_off;   // float[n_partials]: per-tile dalpha partial sums
   size_t n_partials;
   size_t total;

@@ -188,6 +188,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            bytes, 0x00020000);
 }
 
+// A slab as a plain (base, byte length) pair; the buffer resource is formed
+// where a load is issued.
+struct Slab {
+  const uint16_t* p;
+  uint32_t bytes;
+};
+
 __device__ __forceinline__ u32x4 bld16(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -199,6 +206,15 @@ __device__ __forceinline__ u32x4 bld16(rsrc_t r, int off) {
 __device__ __forceinline__ int whole(int x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+
+// Within each 16-lane row: lane i takes lane i+1's value (row_shl:1) or lane
+// i-1's value (row_shr:1); lanes whose source lies outside the row get 0.
+__device__ __forceinline__ float row_next(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x101, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_prev(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ uint2 bld8(rsrc_t r, int off) {
@@ -392,10 +408,11 @@ __device__ __forceinline__ TileLane<D> tile_lane(int lane) {
 
 // Issue the loads of rows row0..row0+15 into the LDS block at `dst`. Rows
 // outside the slab are not read (buffer range check).
-template <int D, typename R>
-__device__ __forceinline__ void stage_block(R r, const TileLane<D>& tl,
+template <int D>
+__device__ __forceinline__ void stage_block(Slab sl, const TileLane<D>& tl,
                                             int row0, lds_char* dst) {
   using Tl = Tile<D>;
+  const rsrc_t r = make_rsrc(sl.p, sl.bytes);
 #pragma unroll
   for (int ii = 0; ii < Tl::kLoads; ++ii)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -404,8 +421,8 @@ __device__ __forceinline__ void stage_block(R r, const TileLane<D>& tl,
 
 // Stage rows r0.. and r1.. (INT_MIN: absent) of tensors A and B into the four
 // blocks A_x A_y B_x B_y of an LDS stage.
-template <int D, typename R>
-__device__ __forceinline__ void stage_two(R ra, R rb, const TileLane<D>& tl, int r0,
+template <int D>
+__device__ __forceinline__ void stage_two(Slab ra, Slab rb, const TileLane<D>& tl, int r0,
                                           int r1, lds_char* st) {
   constexpr int kB = Tile<D>::kBlockBytes;
   if (r0 != INT_MIN) {
@@ -494,8 +511,6 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   const size_t base = static_cast<size_t>(bh) * T * D;
   const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
   const rsrc_t rq = make_rsrc(q + base, slab);
-  const rsrc_t rk = make_rsrc(k + base, slab);
-  const rsrc_t rv = make_rsrc(v + base, slab);
   const TileLane<D> tl = tile_lane<D>(lane);
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
@@ -517,7 +532,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
 
   u32x4 qb[D / 32];
   bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
-  stage_two<D>(rk, rv, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+  stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
 
   f32x4 acc[D / 16];
 #pragma unroll
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
 
   for (int p = 0; p < npair; ++p) {
     lds_char* st = lds;
-    if (p > 0) stage_two<D>(rk, rv, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+    if (p > 0) stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     // ---- scores of the pair
@@ -659,8 +674,6 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const size_t base = static_cast<size_t>(bh) * T * D;
   const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
   const rsrc_t rq = make_rsrc(q + base, slab);
-  const rsrc_t rk = make_rsrc(k + base, slab);
-  const rsrc_t rv = make_rsrc(v + base, slab);
   const rsrc_t rg = make_rsrc(dout + base, slab);
   const TileLane<D> tl = tile_lane<D>(lane);
   const int i = i0 + n;
@@ -684,7 +697,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   u32x4 qb[D / 32], gb[D / 32];
   bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
   bload_rows<D>(rg, 16 * g + n * 2 * D, i0, gb);
-  stage_two<D>(rk, rv, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+  stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
 
   f32x4 a1[D / 16], a2[D / 16];
 #pragma unroll
@@ -696,7 +709,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 
   for (int p = 0; p < npair; ++p) {
     lds_char* st = lds;
-    if (p > 0) stage_two<D>(rk, rv, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+    if (p > 0) stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     const bool win = p < nwp;
@@ -775,7 +788,8 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
       *reinterpret_cast<float4*>(o + 16 * mb) =
           make_float4(scale * (a1[mb][0] - Dl * a2[mb][0]), scale * (a1[mb][1] - Dl * a2[mb][1]),
                       scale * (a1[mb][2] - Dl * a2[mb][2]), scale * (a1[mb][3] - Dl * a2[mb][3]));
-    if (g == 0) delta[static_cast<size_t>(bh) * T + i] = Dl;
+    if (g == 0)
+      reinterpret_cast<float2*>(delta)[static_cast<size_t>(bh) * T + i] = make_float2(L2, Dl);
   }
   float dal = (g == 0) ? al_a - Dl * al_b : 0.f;       // al_* are replicated over g
 #pragma unroll
@@ -829,6 +843,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
   const TileLane<D> tl = tile_lane<D>(lane);
   const float scale = pr.scale;
   const float c2 = scale * kLog2e;
+  // per query {lse * log2(e), Delta}, written by the dq stage
+  const rsrc_t rd = make_rsrc(delta + 2 * rbase, static_cast<uint32_t>(T) * 8u);
   // The dq stage has finished (same stream): workgroup 0 also sums its
   // per-tile dalpha partials, in fp64 and a fixed order (lane-strided sums,
   // then a butterfly).
@@ -853,7 +869,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
   u32x4 kb[D / 32], vb[D / 32];
   bload_rows<D>(rk, 16 * g + n * 2 * D, rowb, kb);
   bload_rows<D>(rv, 16 * g + n * 2 * D, rowb, vb);
-  stage_two<D>(rq, rg, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+  stage_two<D>(Slab{q + base, slab}, Slab{dout + base, slab}, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
 
   f32x4 ak[D / 16], av[D / 16];
 #pragma unroll
@@ -866,7 +882,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
 
   for (int p = 0; p < npair; ++p) {
     lds_char* st = lds;
-    if (p > 0) stage_two<D>(rq, rg, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+    if (p > 0) stage_two<D>(Slab{q + base, slab}, Slab{dout + base, slab}, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     const bool win = p < nwp;
@@ -883,33 +899,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
       const f32x4 s = mfma_rows<D>(qa, kb);
       const f32x4 d = mfma_rows<D>(ga, vb);
       if (win) {
+        // {L2, Delta} of queries ib+4g .. ib+4g+3, one 8-byte load each: the
+        // buffer range check rejects a whole access that crosses the slab
+        // edge, so a wider load would lose a valid query next to row -1 or T.
+        float qL[4], qD[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 x = bld8(rd, (ib + 4 * g + j) * 8);
+          qL[j] = __uint_as_float(x.x);
+          qD[j] = __uint_as_float(x.y);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int iq = ib + 4 * g + j;
           const int rel = iq - r;
           const bool ok = iq < T && r >= 0 && rel >= 0 && rel < W;
-          const int ii = clampi(iq, 0, T - 1);
-          const float pe = ok ? ex2(s[j] * c2 - lse[rbase + ii] * kLog2e) : 0.f;
+          const float pe = ok ? ex2(s[j] * c2 - qL[j]) : 0.f;
           pv[4 * hf + j] = pe;
-          dsv[4 * hf + j] = ok ? pe * (d[j] - delta[rbase + ii]) : 0.f;
+          dsv[4 * hf + j] = ok ? pe * (d[j] - qD[j]) : 0.f;
         }
       } else {
         const int t = 2 * (p - nwp) + hf;
         const float wl = taps.w_lo[t], wh = taps.w_hi[t];
+        const uint2 ldq = bld8(rd, (ib + n) * 8);        // {L2, Delta} of query m
         float s_lo = 0.f, s_hi = 0.f, d_lo = 0.f, d_hi = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float su = __shfl_down(s[j], 1, 16);
-          const float du = __shfl_down(d[j], 1, 16);
+          const float su = row_next(s[j]);
+          const float du = row_next(d[j]);
           if (jj == j) { s_lo = s[j]; s_hi = su; d_lo = d[j]; d_hi = du; }
         }
         const int iq = ib + n;
         const bool ok = jj >= 0 && jj < 4 && n < kTileQ && iq < T && iq >= taps.c[t];
-        const int ii = clampi(iq, 0, T - 1);
-        const float pe = ok ? ex2((wl * s_lo + wh * s_hi) * c2 - lse[rbase + ii] * kLog2e) : 0.f;
-        const float ds = ok ? pe * (wl * d_lo + wh * d_hi - delta[rbase + ii]) : 0.f;
-        const float p_up = __shfl_up(pe, 1, 16);        // query m-1's values
-        const float ds_up = __shfl_up(ds, 1, 16);
+        const float pe = ok ? ex2((wl * s_lo + wh * s_hi) * c2 - __uint_as_float(ldq.x)) : 0.f;
+        const float ds = ok ? pe * (wl * d_lo + wh * d_hi - __uint_as_float(ldq.y)) : 0.f;
+        const float p_up = row_prev(pe);                 // query m-1's values
+        const float ds_up = row_prev(ds);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qn = 4 * g + j;                      // query of reg j
