@@ -271,6 +271,10 @@ def main():
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-t4096", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (3 launches), whose "
+                         "FETCH_SIZE/WRITE_SIZE counters scale the kernels' counters "
+                         "to bytes in a rocprofv3 --pmc run")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -284,6 +288,14 @@ def main():
     from static_pattern_sparse_amd import inputs as I
     torch.cuda.set_device(0)
     F.lib()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     wl = I.WORKLOADS["linear16_bwd_bf16_b8h8t1024d64_w12"]
     stack = Stack(wl, 12, args.layers, torch, F, I)
