@@ -100,18 +100,21 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Map the 1-D workgroup id to (head, tile). Workgroups are dispatched
 // round-robin over the 8 XCDs; when the head count allows, all tiles of one
-// head go to one XCD, in order, so the rows its taps re-read stay in that
-// XCD's L2.
+// head go to one XCD, consecutively, so the rows its taps re-read stay in
+// that XCD's L2. Tiles run from the end of the sequence backwards: for the
+// key-side kernel the query rows a tile's taps read lie ahead of it and have
+// then already been fetched by the tiles dispatched before it (measured:
+// dk/dv 71 -> 62 us at T=4096; the forward is indifferent).
 __device__ __forceinline__ void map_tile(int bid, int BH, int n_tiles, int* bh,
                                          int* tile) {
   if ((BH & 7) == 0) {
     const int xcd = bid & 7;
     const int slot = bid >> 3;
     *bh = (slot / n_tiles) * 8 + xcd;
-    *tile = slot % n_tiles;
+    *tile = n_tiles - 1 - slot % n_tiles;
   } else {
     *bh = bid / n_tiles;
-    *tile = bid % n_tiles;
+    *tile = n_tiles - 1 - bid % n_tiles;
   }
 }
 
