@@ -353,13 +353,21 @@ __device__ __forceinline__ LaneMasks lane_masks(int n, int g) {
 // A 16-row block of a row tensor (q, k, v or dout of one slab) is staged in
 // LDS row-major, 2D bytes per row, by fully coalesced 16-byte direct-to-LDS
 // buffer loads (lane l of a load writes bytes 16l.. of the load's 1 KB).
+//
+// LDS of gfx950 (measured with the bank-conflict counter): 64 banks of 4
+// bytes, i.e. one 256-byte bank line; ds_read_b64 and ds_read_b64_tr_b16
+// serve 32 consecutive lanes per cycle; ds_read_b128 serves 16 lanes per
+// cycle, in each half-wave the quads (lane >> 2) whose index has an even
+// number of set bits ({0-3, 12-15, 20-23, 24-27} + 32h), then the others.
 // Within row r the 16-byte chunk c sits at position c ^ swz(r), with
-//   swz(r) = ((r & 3) << 1) | ((r >> 2) & 1),
-// which keeps both read patterns free of bank conflicts:
-//   natural operand  ds_read_b128, lane (g, n): row n, chunk g + 4s
-//                    (8 consecutive rows hit 8 distinct chunk slots);
-//   transposed       ds_read_b64_tr_b16, 16-lane group g: rows 4g'..4g'+3,
-//                    two chunks each (4 rows x 2 chunks -> 8 distinct slots).
+//   swz(r) = 2 * ((r / rows per bank line) mod (chunks per row / 2)),
+// i.e. r & 6 for 128-byte rows and 2 (r & 7) for 256-byte rows, which keeps
+// both read patterns free of bank conflicts:
+//   natural operand  ds_read_b128, lane (g, n): row n, chunk g + 4s;
+//   transposed       ds_read_b64_tr_b16, lanes 0-31: rows 0..7 (4g + n/4),
+//                    one chunk pair {2mb, 2mb + 1} each -- the pair moves as a
+//                    whole (the XOR is even), so 8 rows x 2 chunks fill all
+//                    64 banks.
 // ds_read_b64_tr_b16: within a 16-lane group, lane i receives element
 // i % 4 of the 8 bytes that lane 4e + i/4 points at, for e = 0..3. With lane j
 // pointing at row k0 + j/4, columns 16mb + 4(j%4)..+3, lane i receives
@@ -368,7 +376,10 @@ __device__ __forceinline__ LaneMasks lane_masks(int n, int g) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 64 ? (r & 6) : 2 * (r & 7);
+}
 
 template <int D>
 struct Tile {
@@ -397,15 +408,15 @@ __device__ __forceinline__ TileLane<D> tile_lane(int lane) {
     const int flat = ii * 1024 + 16 * lane;            // LDS byte in the block
     const int r = flat / Tl::kRowBytes;
     const int pos = (flat % Tl::kRowBytes) / 16;
-    t.src[ii] = r * Tl::kRowBytes + 16 * (pos ^ swz(r));
+    t.src[ii] = r * Tl::kRowBytes + 16 * (pos ^ swz<D>(r));
   }
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
-    t.nat[s] = n * Tl::kRowBytes + 16 * ((g + 4 * s) ^ swz(n));
+    t.nat[s] = n * Tl::kRowBytes + 16 * ((g + 4 * s) ^ swz<D>(n));
   const int row = 4 * g + (n >> 2);
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb)
-    t.tr[mb] = row * Tl::kRowBytes + 16 * ((2 * mb + ((n & 3) >> 1)) ^ swz(row)) + 8 * (n & 1);
+    t.tr[mb] = row * Tl::kRowBytes + 16 * ((2 * mb + ((n & 3) >> 1)) ^ swz<D>(row)) + 8 * (n & 1);
   return t;
 }
 
