@@ -498,14 +498,115 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+
+// ---------------------------------------------------------------- tap helpers
+// Tap constants live in lanes: lane t (< kNumTaps) holds tap t's values, and a
+// loop over taps reads them into scalar registers with v_readlane (no memory
+// access inside the loop). Lanes >= kNumTaps hold tap 0's values.
+struct TapLane {
+  int c;
+  float wl, wh, nf;
+};
+
+__device__ __forceinline__ TapLane tap_lane(const Taps& taps, int lane) {
+  TapLane r{taps.c[0], taps.w_lo[0], taps.w_hi[0], taps.neg_f[0]};
+#pragma unroll
+  for (int t = 1; t < kNumTaps; ++t)
+    if (lane == t) r = TapLane{taps.c[t], taps.w_lo[t], taps.w_hi[t], taps.neg_f[t]};
+  return r;
+}
+
+__device__ __forceinline__ int rl_i(int x, int t) { return __builtin_amdgcn_readlane(x, t); }
+__device__ __forceinline__ float rl_f(float x, int t) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
+}
+
+// Number of taps whose lower row lies at or before `last` (the taps are sorted
+// by distance, so they form a prefix).
+__device__ __forceinline__ int taps_upto(const TapLane& tv, int ntaps, int lane, int last) {
+  return __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < ntaps && tv.c <= last));
+}
+
+// Two cross-row (g) sums at once, each left in every lane. permlane16_swap
+// exchanges the odd rows of its first operand with the even rows of its
+// second; permlane32_swap exchanges rows 2-3 of the first with rows 0-1 of the
+// second:
+//   swap16(x, y) -> [x0 y0 x2 y2], [x1 y1 x3 y3]; sum = [x01 y01 x23 y23]
+//   swap32(s, s) -> [s0 s1 s0 s1], [s2 s3 s2 s3]; sum = [X Y X Y]
+//   swap16(t, t) -> [X X X X], [Y Y Y Y].
+__device__ __forceinline__ void rsum4x2(float* x, float* y) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(*x), __float_as_uint(*y), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  const float t = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+  *x = __uint_as_float(c[0]);
+  *y = __uint_as_float(c[1]);
+}
+
+// P operand of a tap pair. In lane (g, n), k-slot j of a block is row 4g + j;
+// query n takes weight a on row n and b on row n + 1 of the block, so each
+// slot holds a, b or 0. One v_perm per dword picks the upper half (the bf16
+// truncation) of a or b, or zero, per 16-bit slot:
+//   selector bytes 2,3 -> src1 (a), 6,7 -> src0 (b), 0x0c -> 0x00.
+struct TapSel {
+  uint32_t s01, s23;   // dwords with slots (0, 1) and (2, 3)
+};
+
+__device__ __forceinline__ TapSel tap_sel(int n, int g) {
+  uint32_t code[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    code[j] = (4 * g + j == n) ? 0x0302u : ((4 * g + j == n + 1) ? 0x0706u : 0x0c0cu);
+  return TapSel{code[0] | (code[1] << 16), code[2] | (code[3] << 16)};
+}
+
+// B operands (hi and lo bf16 parts) of a tap pair with weights (ax, bx) for
+// block X and (ay, by) for block Y: hi is the truncation, lo the truncation of
+// the remainder, so hi + lo carries each weight to about 2^-16 relative.
+__device__ __forceinline__ void tap_operands(float ax, float bx, float ay, float by,
+                                             const TapSel& ts, u32x4* hi, u32x4* lo) {
+  const uint32_t uax = __float_as_uint(ax), ubx = __float_as_uint(bx);
+  const uint32_t uay = __float_as_uint(ay), uby = __float_as_uint(by);
+  const uint32_t rax = __float_as_uint(ax - __uint_as_float(uax & 0xffff0000u));
+  const uint32_t rbx = __float_as_uint(bx - __uint_as_float(ubx & 0xffff0000u));
+  const uint32_t ray = __float_as_uint(ay - __uint_as_float(uay & 0xffff0000u));
+  const uint32_t rby = __float_as_uint(by - __uint_as_float(uby & 0xffff0000u));
+  (*hi)[0] = __builtin_amdgcn_perm(ubx, uax, ts.s01);
+  (*hi)[1] = __builtin_amdgcn_perm(ubx, uax, ts.s23);
+  (*hi)[2] = __builtin_amdgcn_perm(uby, uay, ts.s01);
+  (*hi)[3] = __builtin_amdgcn_perm(uby, uay, ts.s23);
+  (*lo)[0] = __builtin_amdgcn_perm(rbx, rax, ts.s01);
+  (*lo)[1] = __builtin_amdgcn_perm(rbx, rax, ts.s23);
+  (*lo)[2] = __builtin_amdgcn_perm(rby, ray, ts.s01);
+  (*lo)[3] = __builtin_amdgcn_perm(rby, ray, ts.s23);
+}
+
+// Masked parts of a tap block's scores in lane (g, n): the lower-row term
+// (row n) and the upper-row term (row n + 1); the cross-row sum completes them.
+__device__ __forceinline__ float tap_part(const f32x4& s, const LaneMasks& lm, float wl, float wh) {
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo = fmaf(lm.mlo[j], s[j], lo);
+    hi = fmaf(lm.mhi[j], s[j], hi);
+  }
+  return wl * lo + wh * hi;
+}
+
 // ---------------------------------------------------------------- forward
-// One wavefront per 15-query tile. Key blocks are taken in pairs (window pairs
-// first, then tap pairs); K and V of a pair are staged in the wavefront's LDS
-// region (8 KB at D = 64), then consumed. One stage per wavefront keeps the
-// LDS footprint small, so that many wavefronts per CU hide the load latency
-// (a two-stage ring with the next pair in flight measured slower: it halves
-// the resident wavefronts). Softmax is online over the pairs: running max m
-// and sum l (log2 units), the partial output rescaled when m grows.
+// One wavefront per 15-query tile. Key blocks are taken in pairs: the window
+// pairs first, then the tap pairs; K and V of a pair are staged in the
+// wavefront's LDS region (8 KB at D = 64), then consumed. One stage per
+// wavefront keeps the LDS footprint small, so that many wavefronts per CU hide
+// the load latency (a two-stage ring with the next pair in flight measured
+// slower: it halves the resident wavefronts).
+//
+// Softmax is online, in log2 units: running max m and sum l per query. The
+// window pairs update m exactly. In the tap pairs every lane of column n holds
+// query n's score, and m is raised only when a score passes it by more than
+// 2^kLazy (weights up to 2^kLazy are summed as they are): the rescale of the
+// accumulators is then rare, and l, the output and lse stay exact.
 template <int D>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -514,6 +615,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;         // K_x K_y V_x V_y
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLazy = 8.f;
   __shared__ __attribute__((aligned(16))) char smem[kStage];
   lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
@@ -525,118 +627,124 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   const size_t base = static_cast<size_t>(bh) * T * D;
   const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
   const rsrc_t rq = make_rsrc(q + base, slab);
+  const Slab sk{k + base, slab}, sv{v + base, slab};
   const TileLane<D> tl = tile_lane<D>(lane);
+  const TapLane tv = tap_lane(taps, lane);
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
   const float c2 = pr.scale * kLog2e;                 // scores in log2 units
   const LaneMasks lm = lane_masks(n, g);
   const int nwb = (W + kTileQ - 1) / 16 + 1;
-  const int last = min(i0 + kTileQ - 1, T - 1);
-  int ntap = 0;
-  while (ntap < taps.n && taps.c[ntap] <= last) ++ntap;
   const int nwp = (nwb + 1) / 2;
-  const int npair = nwp + (ntap + 1) / 2;
+  const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
 
   zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
 
-  // rows of block hf of pair p (INT_MIN: no block): window blocks i0-16b,
-  // then taps i0-c_t
-#define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nwb, i0, -16, ntap, i0, -1, taps)
-
   u32x4 qb[D / 32];
   bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
-  stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+  stage_two<D>(sk, sv, tl, i0, nwb > 1 ? i0 - 16 : INT_MIN, lds);
 
   f32x4 acc[D / 16];
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  for (int p = 0; p < npair; ++p) {
-    lds_char* st = lds;
-    if (p > 0) stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+  // ---- window pairs: blocks i0 - 16b, b = 2p, 2p + 1
+  for (int p = 0; p < nwp; ++p) {
+    if (p > 0)
+      stage_two<D>(sk, sv, tl, i0 - 32 * p, 2 * p + 1 < nwb ? i0 - 32 * p - 16 : INT_MIN, lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    // ---- scores of the pair
-    float sv[2][4];
+    float sc[2][4];
     float lmax = -INFINITY;
-    const bool win = p < nwp;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sv[hf][j] = -INFINITY;
-      const int r0 = BLOCK_ROW(p, hf);
-      if (r0 == INT_MIN) continue;
+      const int b = 2 * p + hf;
       u32x4 ka[D / 32];
-      nat_operand<D>(st + hf * Tl::kBlockBytes, tl, ka);
+      nat_operand<D>(lds + hf * Tl::kBlockBytes, tl, ka);
       const f32x4 s = mfma_rows<D>(ka, qb);
-      if (win) {
-        const int b = 2 * p + hf;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rel = 4 * g + j - 16 * b;          // key - i0
-          const bool ok = qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
-          sv[hf][j] = ok ? s[j] * c2 : -INFINITY;
-          lmax = fmaxf(lmax, sv[hf][j]);
-        }
-      } else {
-        const int t = 2 * (p - nwp) + hf;
-        float slo = 0.f, shi = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          slo = fmaf(lm.mlo[j], s[j], slo);
-          shi = fmaf(lm.mhi[j], s[j], shi);
-        }
-        const float sc = rsum4(taps.w_lo[t] * slo + taps.w_hi[t] * shi) * c2;
-        sv[hf][0] = (qvalid && i >= taps.c[t]) ? sc : -INFINITY;
-        lmax = fmaxf(lmax, sv[hf][0]);
+      for (int j = 0; j < 4; ++j) {
+        const int rel = 4 * g + j - 16 * b;            // key - i0
+        const bool ok = b < nwb && qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
+        sc[hf][j] = ok ? s[j] * c2 : -INFINITY;
+        lmax = fmaxf(lmax, sc[hf][j]);
       }
     }
-    // ---- online softmax update
     lmax = rmax4(lmax);
     const float mn = fmaxf(m, lmax);
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float corr = ex2(m - ms);                    // 0 when m = -inf
     float pv[8];
     float ladd = 0.f;
-    if (win) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pv[4 * hf + j] = ex2(sv[hf][j] - ms);
-          ladd += pv[4 * hf + j];
-        }
-      ladd = rsum4(ladd);
-    } else {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int t = 2 * (p - nwp) + hf;
-        const int tt = t < ntap ? t : 0;
-        const float pt = ex2(sv[hf][0] - ms);
-        ladd += pt;
-        const float a = pt * taps.w_lo[tt], bb = pt * taps.w_hi[tt];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pv[4 * hf + j] = a * lm.mlo[j] + bb * lm.mhi[j];
-      }
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = ex2(sc[e >> 2][e & 3] - ms);
+      ladd += pv[e];
     }
-    l = l * corr + ladd;
+    l = l * corr + rsum4(ladd);
     m = mn;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[mb][j] *= corr;
-    // ---- P.V of the pair
     u32x4 bhi, blo;
     split8(pv, &bhi, &blo);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 a = tr_operand<D>(st + 2 * Tl::kBlockBytes, st + 3 * Tl::kBlockBytes, tl, mb);
+      const u32x4 a = tr_operand<D>(lds + 2 * Tl::kBlockBytes, lds + 3 * Tl::kBlockBytes, tl, mb);
       acc[mb] = mfma(a, bhi, acc[mb]);
       acc[mb] = mfma(a, blo, acc[mb]);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                // reads of stage done
+    __builtin_amdgcn_wave_barrier();
+  }
+  // a query with no entry (outside the sequence) keeps finite exponents
+  if (m == -INFINITY) m = 0.f;
+
+  // ---- tap pairs: blocks i0 - c_t, t = 2tp, 2tp + 1
+  const TapSel ts = tap_sel(n, g);
+  for (int tp = 0; 2 * tp < ntap; ++tp) {
+    const int t0 = 2 * tp, t1 = t0 + 1;
+    const bool has1 = t1 < ntap;
+    const int c0 = rl_i(tv.c, t0), c1 = rl_i(tv.c, t1);
+    const float wl0 = rl_f(tv.wl, t0), wh0 = rl_f(tv.wh, t0);
+    const float wl1 = rl_f(tv.wl, t1), wh1 = rl_f(tv.wh, t1);
+    stage_two<D>(sk, sv, tl, i0 - c0, has1 ? i0 - c1 : INT_MIN, lds);
+    wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    u32x4 ka[D / 32];
+    nat_operand<D>(lds, tl, ka);
+    const f32x4 s0 = mfma_rows<D>(ka, qb);
+    nat_operand<D>(lds + Tl::kBlockBytes, tl, ka);
+    const f32x4 s1 = mfma_rows<D>(ka, qb);
+    float x0 = tap_part(s0, lm, wl0, wh0), x1 = tap_part(s1, lm, wl1, wh1);
+    rsum4x2(&x0, &x1);
+    const float sc0 = (qvalid && i >= c0) ? x0 * c2 : -INFINITY;
+    const float sc1 = (qvalid && has1 && i >= c1) ? x1 * c2 : -INFINITY;
+    const float mx = fmaxf(sc0, sc1);
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
+      const float mn = fmaxf(m, mx);
+      const float corr = ex2(m - mn);
+      l *= corr;
+      m = mn;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mb][j] *= corr;
+    }
+    const float p0 = ex2(sc0 - m), p1 = ex2(sc1 - m);
+    l += p0 + p1;
+    u32x4 bhi, blo;
+    tap_operands(p0 * wl0, p0 * wh0, p1 * wl1, p1 * wh1, ts, &bhi, &blo);
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      const u32x4 a = tr_operand<D>(lds + 2 * Tl::kBlockBytes, lds + 3 * Tl::kBlockBytes, tl, mb);
+      acc[mb] = mfma(a, bhi, acc[mb]);
+      acc[mb] = mfma(a, blo, acc[mb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
   }
 
@@ -651,7 +759,6 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   }
 }
 
-#undef BLOCK_ROW
 // ---------------------------------------------------------------- backward
 // Query side: one wavefront per 15-query tile, the forward's key blocks and
 // pair loop (K and V of a pair staged in LDS). For each attended entry
