@@ -508,12 +508,31 @@ struct TapLane {
   float wl, wh, nf;
 };
 
-__device__ __forceinline__ TapLane tap_lane(const Taps& taps, int lane) {
-  TapLane r{taps.c[0], taps.w_lo[0], taps.w_hi[0], taps.neg_f[0]};
-#pragma unroll
-  for (int t = 1; t < kNumTaps; ++t)
-    if (lane == t) r = TapLane{taps.c[t], taps.w_lo[t], taps.w_hi[t], taps.neg_f[t]};
-  return r;
+// Lane L of x takes the scalar v (v_writelane_b32 with an inline-constant
+// lane index).
+template <int L>
+__device__ __forceinline__ void write_lane(int* x, int v) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(*x) : "s"(v), "n"(L));
+}
+
+template <int L>
+__device__ __forceinline__ void fill_tap_lanes(const Taps& taps, int* c, int* wl, int* wh, int* nf) {
+  if constexpr (L < kNumTaps) {
+    write_lane<L>(c, taps.c[L]);
+    write_lane<L>(wl, __float_as_int(taps.w_lo[L]));
+    write_lane<L>(wh, __float_as_int(taps.w_hi[L]));
+    write_lane<L>(nf, __float_as_int(taps.neg_f[L]));
+    fill_tap_lanes<L + 1>(taps, c, wl, wh, nf);
+  }
+}
+
+// Built with v_writelane (one per tap and field), so that the compiler does
+// not turn a per-lane select into an indexed copy of the argument block.
+__device__ __forceinline__ TapLane tap_lane(const Taps& taps) {
+  int c = taps.c[0], wl = __float_as_int(taps.w_lo[0]);
+  int wh = __float_as_int(taps.w_hi[0]), nf = __float_as_int(taps.neg_f[0]);
+  fill_tap_lanes<1>(taps, &c, &wl, &wh, &nf);
+  return TapLane{c, __int_as_float(wl), __int_as_float(wh), __int_as_float(nf)};
 }
 
 __device__ __forceinline__ int rl_i(int x, int t) { return __builtin_amdgcn_readlane(x, t); }
@@ -629,7 +648,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   const rsrc_t rq = make_rsrc(q + base, slab);
   const Slab sk{k + base, slab}, sv{v + base, slab};
   const TileLane<D> tl = tile_lane<D>(lane);
-  const TapLane tv = tap_lane(taps, lane);
+  const TapLane tv = tap_lane(taps);
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
   const float c2 = pr.scale * kLog2e;                 // scores in log2 units
@@ -772,7 +791,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
 // i - alpha*f (Depth-Staggered Fibonacci Spacing, Methodology > Architecture
 // and attention > Implementation),
 //   -f * [dS * scale * q.(K[a+1]-K[a]) + p * dout.(V[a+1]-V[a])]
-// = A - Delta_i * B with A, B accumulated per query. The wavefront writes
+// = A - Delta_i * B with A and B accumulated per lane. The wavefront writes
 // Delta_i, dq, and one dalpha partial.
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
@@ -796,7 +815,9 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
   const rsrc_t rq = make_rsrc(q + base, slab);
   const rsrc_t rg = make_rsrc(dout + base, slab);
+  const Slab sk{k + base, slab}, sv{v + base, slab};
   const TileLane<D> tl = tile_lane<D>(lane);
+  const TapLane tv = tap_lane(taps);
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
   const float scale = pr.scale;
@@ -804,21 +825,16 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const float L2 = qvalid ? lse[static_cast<size_t>(bh) * T + i] * kLog2e : 0.f;
   const LaneMasks lm = lane_masks(n, g);
   const int nwb = (W + kTileQ - 1) / 16 + 1;
-  const int last = min(i0 + kTileQ - 1, T - 1);
-  int ntap = 0;
-  while (ntap < taps.n && taps.c[ntap] <= last) ++ntap;
   const int nwp = (nwb + 1) / 2;
-  const int npair = nwp + (ntap + 1) / 2;
+  const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
 
   zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);
 
-#define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nwb, i0, -16, ntap, i0, -1, taps)
-
   u32x4 qb[D / 32], gb[D / 32];
   bload_rows<D>(rq, 16 * g + n * 2 * D, i0, qb);
   bload_rows<D>(rg, 16 * g + n * 2 * D, i0, gb);
-  stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+  stage_two<D>(sk, sv, tl, i0, nwb > 1 ? i0 - 16 : INT_MIN, lds);
 
   f32x4 a1[D / 16], a2[D / 16];
 #pragma unroll
@@ -828,62 +844,29 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   }
   float dwin = 0.f, dtap = 0.f, al_a = 0.f, al_b = 0.f;
 
-  for (int p = 0; p < npair; ++p) {
-    lds_char* st = lds;
-    if (p > 0) stage_two<D>(Slab{k + base, slab}, Slab{v + base, slab}, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+  // ---- window pairs: blocks i0 - 16b, b = 2p, 2p + 1
+  for (int p = 0; p < nwp; ++p) {
+    if (p > 0)
+      stage_two<D>(sk, sv, tl, i0 - 32 * p, 2 * p + 1 < nwb ? i0 - 32 * p - 16 : INT_MIN, lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    const bool win = p < nwp;
     float w1[8], w2[8];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { w1[4 * hf + j] = 0.f; w2[4 * hf + j] = 0.f; }
-      const int r0 = BLOCK_ROW(p, hf);
-      if (r0 == INT_MIN) continue;
+      const int b = 2 * p + hf;
       u32x4 ka[D / 32], va[D / 32];
-      nat_operand<D>(st + hf * Tl::kBlockBytes, tl, ka);
-      nat_operand<D>(st + (2 + hf) * Tl::kBlockBytes, tl, va);
+      nat_operand<D>(lds + hf * Tl::kBlockBytes, tl, ka);
+      nat_operand<D>(lds + (2 + hf) * Tl::kBlockBytes, tl, va);
       const f32x4 s = mfma_rows<D>(ka, qb);
       const f32x4 d = mfma_rows<D>(va, gb);
-      if (win) {
-        const int b = 2 * p + hf;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rel = 4 * g + j - 16 * b;
-          const bool ok = qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
-          const float pe = ok ? ex2(s[j] * c2 - L2) : 0.f;
-          w1[4 * hf + j] = pe * d[j];
-          w2[4 * hf + j] = pe;
-          dwin += pe * d[j];
-        }
-      } else {
-        const int t = 2 * (p - nwp) + hf;
-        const float wl = taps.w_lo[t], wh = taps.w_hi[t];
-        float slo = 0.f, shi = 0.f, dlo = 0.f, dhi = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          slo = fmaf(lm.mlo[j], s[j], slo);
-          shi = fmaf(lm.mhi[j], s[j], shi);
-          dlo = fmaf(lm.mlo[j], d[j], dlo);
-          dhi = fmaf(lm.mhi[j], d[j], dhi);
-        }
-        const float ps = rsum4(wl * slo + wh * shi);
-        const float pd = rsum4(wl * dlo + wh * dhi);
-        const float sdf = rsum4(shi - slo);
-        const float gdf = rsum4(dhi - dlo);
-        const bool ok = qvalid && i >= taps.c[t];
-        const float pe = ok ? ex2(ps * c2 - L2) : 0.f;
-        dtap += pe * pd;
-        const float nf = taps.neg_f[t];
-        al_a += nf * pe * (pd * scale * sdf + gdf);
-        al_b += nf * pe * scale * sdf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float wt = wl * lm.mlo[j] + wh * lm.mhi[j];
-          w1[4 * hf + j] = pe * pd * wt;
-          w2[4 * hf + j] = pe * wt;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int rel = 4 * g + j - 16 * b;
+        const bool ok = b < nwb && qvalid && rel <= n && rel > n - W && i0 + rel >= 0;
+        const float pe = ok ? ex2(s[j] * c2 - L2) : 0.f;
+        w1[4 * hf + j] = pe * d[j];
+        w2[4 * hf + j] = pe;
+        dwin += pe * d[j];
       }
     }
     u32x4 h1, l1, h2, l2;
@@ -891,7 +874,67 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     split8(w2, &h2, &l2);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 a = tr_operand<D>(st, st + Tl::kBlockBytes, tl, mb);
+      const u32x4 a = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
+      a1[mb] = mfma(a, h1, a1[mb]);
+      a1[mb] = mfma(a, l1, a1[mb]);
+      a2[mb] = mfma(a, h2, a2[mb]);
+      a2[mb] = mfma(a, l2, a2[mb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- tap pairs: blocks i0 - c_t, t = 2tp, 2tp + 1. The alpha-gradient
+  // terms are kept as per-lane parts (the masked lower/upper row terms of
+  // lane (g, n)); they are linear in those parts, so the final sum over all
+  // lanes completes them without a cross-row sum per entry.
+  const TapSel ts = tap_sel(n, g);
+  float dm[4];                                          // mhi - mlo
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dm[j] = lm.mhi[j] - lm.mlo[j];
+  for (int tp = 0; 2 * tp < ntap; ++tp) {
+    const int t0 = 2 * tp, t1 = t0 + 1;
+    const bool has1 = t1 < ntap;
+    const int c0 = rl_i(tv.c, t0), c1 = rl_i(tv.c, t1);
+    const float wl0 = rl_f(tv.wl, t0), wh0 = rl_f(tv.wh, t0);
+    const float wl1 = rl_f(tv.wl, t1), wh1 = rl_f(tv.wh, t1);
+    const float nf0 = rl_f(tv.nf, t0), nf1 = rl_f(tv.nf, t1);
+    stage_two<D>(sk, sv, tl, i0 - c0, has1 ? i0 - c1 : INT_MIN, lds);
+    wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    u32x4 ka[D / 32];
+    nat_operand<D>(lds, tl, ka);
+    const f32x4 s0 = mfma_rows<D>(ka, qb);
+    nat_operand<D>(lds + Tl::kBlockBytes, tl, ka);
+    const f32x4 s1 = mfma_rows<D>(ka, qb);
+    nat_operand<D>(lds + 2 * Tl::kBlockBytes, tl, ka);
+    const f32x4 d0 = mfma_rows<D>(ka, gb);
+    nat_operand<D>(lds + 3 * Tl::kBlockBytes, tl, ka);
+    const f32x4 d1 = mfma_rows<D>(ka, gb);
+    float ps0 = tap_part(s0, lm, wl0, wh0), ps1 = tap_part(s1, lm, wl1, wh1);
+    float pd0 = tap_part(d0, lm, wl0, wh0), pd1 = tap_part(d1, lm, wl1, wh1);
+    float sdf0 = 0.f, sdf1 = 0.f, gdf0 = 0.f, gdf1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sdf0 = fmaf(dm[j], s0[j], sdf0);
+      sdf1 = fmaf(dm[j], s1[j], sdf1);
+      gdf0 = fmaf(dm[j], d0[j], gdf0);
+      gdf1 = fmaf(dm[j], d1[j], gdf1);
+    }
+    rsum4x2(&ps0, &ps1);
+    rsum4x2(&pd0, &pd1);
+    const float pe0 = (qvalid && i >= c0) ? ex2(ps0 * c2 - L2) : 0.f;
+    const float pe1 = (qvalid && has1 && i >= c1) ? ex2(ps1 * c2 - L2) : 0.f;
+    dtap += pe0 * pd0 + pe1 * pd1;
+    al_a += nf0 * pe0 * (pd0 * scale * sdf0 + gdf0) + nf1 * pe1 * (pd1 * scale * sdf1 + gdf1);
+    al_b += nf0 * pe0 * sdf0 + nf1 * pe1 * sdf1;
+    u32x4 h1, l1, h2, l2;
+    const float q0 = pe0 * pd0, q1 = pe1 * pd1;
+    tap_operands(q0 * wl0, q0 * wh0, q1 * wl1, q1 * wh1, ts, &h1, &l1);
+    tap_operands(pe0 * wl0, pe0 * wh0, pe1 * wl1, pe1 * wh1, ts, &h2, &l2);
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      const u32x4 a = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
       a1[mb] = mfma(a, h1, a1[mb]);
       a1[mb] = mfma(a, l1, a1[mb]);
       a2[mb] = mfma(a, h2, a2[mb]);
@@ -912,13 +955,12 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     if (g == 0)
       reinterpret_cast<float2*>(delta)[static_cast<size_t>(bh) * T + i] = make_float2(L2, Dl);
   }
-  float dal = (g == 0) ? al_a - Dl * al_b : 0.f;       // al_* are replicated over g
+  float dal = al_a - Dl * (scale * al_b);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) dal += __shfl_xor(dal, off);
   if (lane == 0) partials[blockIdx.x] = dal;
 }
 
-#undef BLOCK_ROW
 // Key side: one wavefront per tile of kTileK = 14 key rows j0..j0+13, handled
 // as the 16-row block rowb = j0-1 .. j0+14 (the two end rows are halos whose
 // sums are discarded). Row r of the block collects
