@@ -202,6 +202,18 @@ __device__ __forceinline__ u32x4 bld16(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Streaming (non-temporal) variant for rows read once per launch, so that
+// they do not displace the rows the taps re-read from L2.
+__device__ __forceinline__ u32x4 bld16_nt(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
+// Non-temporal stores of the fp32 results (written once, never re-read by
+// the launch).
+__device__ __forceinline__ void st4_nt(float* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
+}
+
 // Keep a byte offset whole in the VGPR operand: a constant part folded into
 // the instruction's immediate field would be checked together with a negative
 // VGPR part, so a row >= 0 reached from a negative block start is loaded with
@@ -272,7 +284,7 @@ template <int D>
 __device__ __forceinline__ void bload_rows(rsrc_t r, int lane_a, int row0, u32x4* a) {
   const int off = lane_a + row0 * (2 * D);
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) a[s] = bld16(r, off + 64 * s);
+  for (int s = 0; s < D / 32; ++s) a[s] = bld16_nt(r, off + 64 * s);
 }
 
 template <int D>
@@ -390,33 +402,43 @@ struct Tile {
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;
 };
 
-// Per-lane byte offsets, fixed for the whole kernel.
+// Per-lane byte offsets, fixed for the whole kernel. The swizzle XORs chunk
+// bits only, so the offsets of a family differ from their first member in bit
+// fields that the row part never touches:
+//   natural read, k-step s:   nat0 ^ 64 s
+//   transposed read, d-block: tr0 ^ 32 mb
+//   load ii of a block:       src0 + 1024 ii           (128-byte rows)
+//                             (src0 ^ 128 (ii & 1)) + 1024 ii (256-byte rows)
+// and three registers hold them all.
 template <int D>
 struct TileLane {
-  int src[Tile<D>::kLoads];   // global offset (w.r.t. the block's first row)
-  int nat[D / 32];            // natural operand read, k-step s
-  int tr[D / 16];             // transposed read, d-block mb (rows 4g..4g+3)
+  int src0, nat0, tr0;
+  __device__ __forceinline__ int src(int ii) const {
+    return (D == 64 ? src0 : (src0 ^ (128 * (ii & 1)))) + 1024 * ii;
+  }
+  __device__ __forceinline__ int nat(int s) const { return nat0 ^ (64 * s); }
+  __device__ __forceinline__ int tr(int mb) const { return tr0 ^ (32 * mb); }
 };
+
+// The same offsets, marked as changed so that the offsets derived from them
+// are formed where they are used, not hoisted out of a loop into registers.
+template <int D>
+__device__ __forceinline__ TileLane<D> refresh(TileLane<D> t) {
+  asm volatile("" : "+v"(t.nat0), "+v"(t.tr0));
+  return t;
+}
 
 template <int D>
 __device__ __forceinline__ TileLane<D> tile_lane(int lane) {
   using Tl = Tile<D>;
   TileLane<D> t;
   const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ii = 0; ii < Tl::kLoads; ++ii) {
-    const int flat = ii * 1024 + 16 * lane;            // LDS byte in the block
-    const int r = flat / Tl::kRowBytes;
-    const int pos = (flat % Tl::kRowBytes) / 16;
-    t.src[ii] = r * Tl::kRowBytes + 16 * (pos ^ swz<D>(r));
-  }
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-    t.nat[s] = n * Tl::kRowBytes + 16 * ((g + 4 * s) ^ swz<D>(n));
+  const int r = 16 * lane / Tl::kRowBytes;             // row of load 0
+  const int pos = (16 * lane % Tl::kRowBytes) / 16;
+  t.src0 = r * Tl::kRowBytes + 16 * (pos ^ swz<D>(r));
+  t.nat0 = n * Tl::kRowBytes + 16 * (g ^ swz<D>(n));
   const int row = 4 * g + (n >> 2);
-#pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb)
-    t.tr[mb] = row * Tl::kRowBytes + 16 * ((2 * mb + ((n & 3) >> 1)) ^ swz<D>(row)) + 8 * (n & 1);
+  t.tr0 = row * Tl::kRowBytes + 16 * (((n & 3) >> 1) ^ swz<D>(row)) + 8 * (n & 1);
   return t;
 }
 
@@ -430,7 +452,7 @@ __device__ __forceinline__ void stage_block(Slab sl, const TileLane<D>& tl,
 #pragma unroll
   for (int ii = 0; ii < Tl::kLoads; ++ii)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, dst + ii * 1024, 16, whole(row0 * Tl::kRowBytes + tl.src[ii]), 0, 0, 0);
+        r, dst + ii * 1024, 16, whole(row0 * Tl::kRowBytes + tl.src(ii)), 0, 0, 0);
 }
 
 // Stage rows r0.. and r1.. (INT_MIN: absent) of tensors A and B into the four
@@ -467,7 +489,7 @@ __device__ __forceinline__ void nat_operand(const lds_char* blk, const TileLane<
                                             u32x4* a) {
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
-    a[s] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(blk + tl.nat[s]);
+    a[s] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(blk + tl.nat(s));
 }
 
 // A operand X^T for d-block mb over a pair of blocks (x rows 4g..4g+3 then y).
@@ -475,9 +497,9 @@ template <int D>
 __device__ __forceinline__ u32x4 tr_operand(const lds_char* x, const lds_char* y,
                                             const TileLane<D>& tl, int mb) {
   const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(x + tl.tr[mb]));
+      (__attribute__((address_space(3))) v4i16*)(x + tl.tr(mb)));
   const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(y + tl.tr[mb]));
+      (__attribute__((address_space(3))) v4i16*)(y + tl.tr(mb)));
   const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
   u32x4 r;
   r[0] = ua.x; r[1] = ua.y; r[2] = ub.x; r[3] = ub.y;
@@ -772,9 +794,9 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     float* o = out + base + static_cast<size_t>(i) * D + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb)
-      *reinterpret_cast<float4*>(o + 16 * mb) =
-          make_float4(acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv);
-    if (g == 0) lse[static_cast<size_t>(bh) * T + i] = (m + lg2(l)) * 0.6931471805599453f;
+      st4_nt(o + 16 * mb, acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv);
+    if (g == 0)
+      __builtin_nontemporal_store((m + lg2(l)) * 0.6931471805599453f, lse + static_cast<size_t>(bh) * T + i);
   }
 }
 
@@ -949,9 +971,8 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     float* o = dq + base + static_cast<size_t>(i) * D + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb)
-      *reinterpret_cast<float4*>(o + 16 * mb) =
-          make_float4(scale * (a1[mb][0] - Dl * a2[mb][0]), scale * (a1[mb][1] - Dl * a2[mb][1]),
-                      scale * (a1[mb][2] - Dl * a2[mb][2]), scale * (a1[mb][3] - Dl * a2[mb][3]));
+      st4_nt(o + 16 * mb, scale * (a1[mb][0] - Dl * a2[mb][0]), scale * (a1[mb][1] - Dl * a2[mb][1]),
+             scale * (a1[mb][2] - Dl * a2[mb][2]), scale * (a1[mb][3] - Dl * a2[mb][3]));
     if (g == 0)
       reinterpret_cast<float2*>(delta)[static_cast<size_t>(bh) * T + i] = make_float2(L2, Dl);
   }
@@ -973,9 +994,30 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 // Query and dout blocks of a pair are staged in LDS;
 // scores are recomputed as S = Q_blk K^T (query rows natural from LDS as A,
 // the tile's key rows as B in registers), so lane (g, m) holds query 4g+j
-// against key m and a tap score needs lanes m and m+1 of one 16-lane row.
+// against key m. For a tap block, query n' = 4g + jj (jj = m - 4g) lives in
+// lane (g, m = n') register jj: its lower-row score is that register, its
+// upper-row score register jj of lane m + 1 (one row shift).
 // dk^T += Q_blk^T (W o dS) and dv^T += dout_blk^T (W o P) read Q^T and dout^T
 // transposed from the same LDS tiles.
+
+// Select register j of a C fragment, j = 2*b1 + b0 given as lane masks.
+__device__ __forceinline__ float pick4(const f32x4& x, bool b0, bool b1) {
+  const float lo = b0 ? x[1] : x[0];
+  const float hi = b0 ? x[3] : x[2];
+  return b1 ? hi : lo;
+}
+
+// P operand selectors of a key-side tap block: lane (g, m) places its own
+// query's weight a at slot jj = m - 4g and the previous lane's weight b (query
+// m - 1, for which row m is the upper row) at slot jj - 1.
+__device__ __forceinline__ TapSel key_tap_sel(int n, int g) {
+  const int jj = n - 4 * g;
+  uint32_t code[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) code[j] = (j == jj) ? 0x0302u : ((j == jj - 1) ? 0x0706u : 0x0c0cu);
+  return TapSel{code[0] | (code[1] << 16), code[2] | (code[3] << 16)};
+}
+
 template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -986,7 +1028,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
     float* __restrict__ dalpha) {
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // Q_x Q_y G_x G_y
-  constexpr float kLog2e = 1.4426950408889634f;
   __shared__ __attribute__((aligned(16))) char smem[kStage];
   lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x;
@@ -999,13 +1040,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
   const size_t base = static_cast<size_t>(bh) * T * D;
   const size_t rbase = static_cast<size_t>(bh) * T;
   const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
-  const rsrc_t rq = make_rsrc(q + base, slab);
   const rsrc_t rk = make_rsrc(k + base, slab);
   const rsrc_t rv = make_rsrc(v + base, slab);
-  const rsrc_t rg = make_rsrc(dout + base, slab);
-  const TileLane<D> tl = tile_lane<D>(lane);
+  const Slab sq{q + base, slab}, sg{dout + base, slab};
+  const TileLane<D> tl_ = tile_lane<D>(lane);
+  const TileLane<D>& tl = tl_;
   const float scale = pr.scale;
-  const float c2 = scale * kLog2e;
+  const float c2 = scale * 1.4426950408889634f;
   // per query {lse * log2(e), Delta}, written by the dq stage
   const rsrc_t rd = make_rsrc(delta + 2 * rbase, static_cast<uint32_t>(T) * 8u);
   // The dq stage has finished (same stream): workgroup 0 also sums its
@@ -1019,20 +1060,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
     if (lane == 0) dalpha[0] = static_cast<float>(acc);
   }
   const int nqb = (W + kTileK + 15) / 16;              // window query blocks
-  int ntap = 0;                                         // taps with a query < T
-  while (ntap < taps.n && j0 + taps.c[ntap] - 1 <= T - 1) ++ntap;
   const int nwp = (nqb + 1) / 2;
-  const int npair = nwp + (ntap + 1) / 2;
+  int ntap = 0;                                         // taps with a query < T
+  while (ntap < taps.n && taps.c[ntap] <= T - j0) ++ntap;
 
   zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);
 
-#define BLOCK_ROW(p, hf) pair_row((p), (hf), nwp, nqb, rowb, 16, ntap, j0 - 1, 1, taps)
-
   u32x4 kb[D / 32], vb[D / 32];
   bload_rows<D>(rk, 16 * g + n * 2 * D, rowb, kb);
   bload_rows<D>(rv, 16 * g + n * 2 * D, rowb, vb);
-  stage_two<D>(Slab{q + base, slab}, Slab{dout + base, slab}, tl, BLOCK_ROW(0, 0), BLOCK_ROW(0, 1), lds);
+  stage_two<D>(sq, sg, tl, rowb, nqb > 1 ? rowb + 16 : INT_MIN, lds);
 
   f32x4 ak[D / 16], av[D / 16];
 #pragma unroll
@@ -1041,69 +1079,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
     av[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int r = rowb + n;                               // this lane's key row
-  const int jj = n - 4 * g;                             // reg holding query m
 
-  for (int p = 0; p < npair; ++p) {
-    lds_char* st = lds;
-    if (p > 0) stage_two<D>(Slab{q + base, slab}, Slab{dout + base, slab}, tl, BLOCK_ROW(p, 0), BLOCK_ROW(p, 1), lds);
+  // ---- window pairs: query blocks rowb + 16b, b = 2p, 2p + 1
+  for (int p = 0; p < nwp; ++p) {
+    if (p > 0)
+      stage_two<D>(sq, sg, tl, rowb + 32 * p, 2 * p + 1 < nqb ? rowb + 32 * p + 16 : INT_MIN, lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    const bool win = p < nwp;
     float pv[8], dsv[8];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { pv[4 * hf + j] = 0.f; dsv[4 * hf + j] = 0.f; }
-      const int ib = BLOCK_ROW(p, hf);
-      if (ib == INT_MIN) continue;
+      const int b = 2 * p + hf;
+      const int ib = rowb + 16 * b;
       u32x4 qa[D / 32], ga[D / 32];
-      nat_operand<D>(st + hf * Tl::kBlockBytes, tl, qa);
-      nat_operand<D>(st + (2 + hf) * Tl::kBlockBytes, tl, ga);
+      nat_operand<D>(lds + hf * Tl::kBlockBytes, tl, qa);
+      nat_operand<D>(lds + (2 + hf) * Tl::kBlockBytes, tl, ga);
       const f32x4 s = mfma_rows<D>(qa, kb);
       const f32x4 d = mfma_rows<D>(ga, vb);
-      if (win) {
-        // {L2, Delta} of queries ib+4g .. ib+4g+3, one 8-byte load each: the
-        // buffer range check rejects a whole access that crosses the slab
-        // edge, so a wider load would lose a valid query next to row -1 or T.
-        float qL[4], qD[4];
+      // {L2, Delta} of queries ib+4g .. ib+4g+3, one 8-byte load each: the
+      // buffer range check rejects a whole access that crosses the slab
+      // edge, so a wider load would lose a valid query next to row -1 or T.
+      float qL[4], qD[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint2 x = bld8(rd, (ib + 4 * g + j) * 8);
-          qL[j] = __uint_as_float(x.x);
-          qD[j] = __uint_as_float(x.y);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const uint2 x = bld8(rd, (ib + 4 * g + j) * 8);
+        qL[j] = __uint_as_float(x.x);
+        qD[j] = __uint_as_float(x.y);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int iq = ib + 4 * g + j;
-          const int rel = iq - r;
-          const bool ok = iq < T && r >= 0 && rel >= 0 && rel < W;
-          const float pe = ok ? ex2(s[j] * c2 - qL[j]) : 0.f;
-          pv[4 * hf + j] = pe;
-          dsv[4 * hf + j] = ok ? pe * (d[j] - qD[j]) : 0.f;
-        }
-      } else {
-        const int t = 2 * (p - nwp) + hf;
-        const float wl = taps.w_lo[t], wh = taps.w_hi[t];
-        const uint2 ldq = bld8(rd, (ib + n) * 8);        // {L2, Delta} of query m
-        float s_lo = 0.f, s_hi = 0.f, d_lo = 0.f, d_hi = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float su = row_next(s[j]);
-          const float du = row_next(d[j]);
-          if (jj == j) { s_lo = s[j]; s_hi = su; d_lo = d[j]; d_hi = du; }
-        }
-        const int iq = ib + n;
-        const bool ok = jj >= 0 && jj < 4 && n < kTileQ && iq < T && iq >= taps.c[t];
-        const float pe = ok ? ex2((wl * s_lo + wh * s_hi) * c2 - __uint_as_float(ldq.x)) : 0.f;
-        const float ds = ok ? pe * (wl * d_lo + wh * d_hi - __uint_as_float(ldq.y)) : 0.f;
-        const float p_up = row_prev(pe);                 // query m-1's values
-        const float ds_up = row_prev(ds);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qn = 4 * g + j;                      // query of reg j
-          pv[4 * hf + j] = n == qn ? wl * pe : (n == qn + 1 ? wh * p_up : 0.f);
-          dsv[4 * hf + j] = n == qn ? wl * ds : (n == qn + 1 ? wh * ds_up : 0.f);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int iq = ib + 4 * g + j;
+        const int rel = iq - r;
+        const bool ok = b < nqb && iq < T && r >= 0 && rel >= 0 && rel < W;
+        const float pe = ok ? ex2(s[j] * c2 - qL[j]) : 0.f;
+        pv[4 * hf + j] = pe;
+        dsv[4 * hf + j] = ok ? pe * (d[j] - qD[j]) : 0.f;
       }
     }
     u32x4 phi, plo, shi, slo;
@@ -1111,10 +1121,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
     split8(dsv, &shi, &slo);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 aq = tr_operand<D>(st, st + Tl::kBlockBytes, tl, mb);
+      const u32x4 aq = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
       ak[mb] = mfma(aq, shi, ak[mb]);
       ak[mb] = mfma(aq, slo, ak[mb]);
-      const u32x4 ag = tr_operand<D>(st + 2 * Tl::kBlockBytes, st + 3 * Tl::kBlockBytes, tl, mb);
+      const u32x4 ag = tr_operand<D>(lds + 2 * Tl::kBlockBytes, lds + 3 * Tl::kBlockBytes, tl, mb);
       av[mb] = mfma(ag, phi, av[mb]);
       av[mb] = mfma(ag, plo, av[mb]);
     }
@@ -1122,20 +1132,86 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
     __builtin_amdgcn_wave_barrier();
   }
 
-  if (n >= 1 && n <= kTileK && r < T) {
-    float* okp = dk + base + static_cast<size_t>(r) * D + 4 * g;
-    float* ovp = dv + base + static_cast<size_t>(r) * D + 4 * g;
+  // ---- tap pairs: query blocks rowb + c_t, t = 2tp, 2tp + 1
+  const TapLane tv = tap_lane(taps);
+  const int jj = n - 4 * g;                             // register of query n
+  const bool diag = jj >= 0 && jj < 4 && n < kTileQ;    // lane holds a query
+  const bool s0b = jj & 1, s1b = jj & 2;                // select register jj
+  const bool u0b = (jj - 1) & 1, u1b = (jj - 1) & 2;    // select register jj - 1
+  const TapSel ks = key_tap_sel(n, g);
+  for (int tp = 0; 2 * tp < ntap; ++tp) {
+    const int t0 = 2 * tp, t1 = t0 + 1;
+    const bool has1 = t1 < ntap;
+    const int c0 = rl_i(tv.c, t0), c1 = rl_i(tv.c, t1);
+    const float wl0 = rl_f(tv.wl, t0), wh0 = rl_f(tv.wh, t0);
+    const float wl1 = rl_f(tv.wl, t1), wh1 = rl_f(tv.wh, t1);
+    const int ib0 = rowb + c0, ib1 = rowb + c1;
+    stage_two<D>(sq, sg, tl, ib0, has1 ? ib1 : INT_MIN, lds);
+    const uint2 ld0 = bld8(rd, (ib0 + n) * 8);          // {L2, Delta} of query n
+    const uint2 ld1 = bld8(rd, (ib1 + n) * 8);
+    wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    const TileLane<D> tl = refresh(tl_);
+    // one block at a time (its four score fragments die before the next
+    // block's are formed)
+    float ps[2], pd[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const float wl = hf ? wl1 : wl0, wh = hf ? wh1 : wh0;
+      u32x4 qa[D / 32];
+      nat_operand<D>(lds + hf * Tl::kBlockBytes, tl, qa);
+      const f32x4 sx = mfma_rows<D>(qa, kb);
+      nat_operand<D>(lds + (2 + hf) * Tl::kBlockBytes, tl, qa);
+      const f32x4 dx = mfma_rows<D>(qa, vb);
+      ps[hf] = wl * pick4(sx, s0b, s1b) + wh * row_next(pick4(sx, u0b, u1b));
+      pd[hf] = wl * pick4(dx, s0b, s1b) + wh * row_next(pick4(dx, u0b, u1b));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float ps0 = ps[0], ps1 = ps[1], pd0 = pd[0], pd1 = pd[1];
+    const int iq0 = ib0 + n, iq1 = ib1 + n;
+    const bool ok0 = diag && iq0 < T && iq0 >= c0;
+    const bool ok1 = diag && has1 && iq1 < T && iq1 >= c1;
+    const float pe0 = ok0 ? ex2(ps0 * c2 - __uint_as_float(ld0.x)) : 0.f;
+    const float pe1 = ok1 ? ex2(ps1 * c2 - __uint_as_float(ld1.x)) : 0.f;
+    const float ds0 = ok0 ? pe0 * (pd0 - __uint_as_float(ld0.y)) : 0.f;
+    const float ds1 = ok1 ? pe1 * (pd1 - __uint_as_float(ld1.y)) : 0.f;
+    // dv first, then dk: one pair of hi/lo operands live at a time
+    u32x4 ohi, olo;
+    tap_operands(wl0 * pe0, wh0 * row_prev(pe0), wl1 * pe1, wh1 * row_prev(pe1), ks, &ohi, &olo);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
-      *reinterpret_cast<float4*>(okp + 16 * mb) =
-          make_float4(ak[mb][0] * scale, ak[mb][1] * scale, ak[mb][2] * scale, ak[mb][3] * scale);
-      *reinterpret_cast<float4*>(ovp + 16 * mb) =
-          make_float4(av[mb][0], av[mb][1], av[mb][2], av[mb][3]);
+      const u32x4 ag = tr_operand<D>(lds + 2 * Tl::kBlockBytes, lds + 3 * Tl::kBlockBytes, tl, mb);
+      av[mb] = mfma(ag, ohi, av[mb]);
+      av[mb] = mfma(ag, olo, av[mb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    tap_operands(wl0 * ds0, wh0 * row_prev(ds0), wl1 * ds1, wh1 * row_prev(ds1), ks, &ohi, &olo);
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      const u32x4 aq = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
+      ak[mb] = mfma(aq, ohi, ak[mb]);
+      ak[mb] = mfma(aq, olo, ak[mb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // output addresses formed here (an opaque copy of the lane index keeps the
+  // compiler from holding them in registers across the loops)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int nn = ln & 15, gg = ln >> 4, rr = rowb + nn;
+  if (nn >= 1 && nn <= kTileK && rr < T) {
+    float* okp = dk + base + static_cast<size_t>(rr) * D + 4 * gg;
+    float* ovp = dv + base + static_cast<size_t>(rr) * D + 4 * gg;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      st4_nt(okp + 16 * mb, ak[mb][0] * scale, ak[mb][1] * scale, ak[mb][2] * scale, ak[mb][3] * scale);
+      st4_nt(ovp + 16 * mb, av[mb][0], av[mb][1], av[mb][2], av[mb][3]);
     }
   }
 }
 
-#undef BLOCK_ROW
 }  // namespace
 
 bool mfma_supported(const Problem& pr, int dtype) {
