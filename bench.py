@@ -10,12 +10,22 @@ layer has its own input and output buffers (about 1.5 GiB in all, more than the
 next. Inputs are seeded N(0,1) synthetic tensors (post-RoPE q, k) and sit in
 HBM before the timed region starts.
 
+A step runs the forward of every layer in layer order, then the backward of
+every layer in reverse order, each as its two stages (dq, Delta and dalpha
+partials; then dk, dv and dalpha); each layer has its own backward workspace.
+ms_per_step and value come from the host clock around the timed steps, with no
+event between launches. The per-kernel times come from a second pass over as
+many steps with a HIP event before every launch, recorded on the launch
+stream. Those events are created without the system-scope fence that a default
+event record issues: that fence writes back and invalidates the caches and
+slows the launch that follows.
+
 value = layers * B * H * T / step time (token-heads per second, every layer
 counted). The JSON line also carries:
   roofline      the dominant kernel's algorithmic bytes per launch divided by
-                its mean launch time (HIP events on the launch stream), against
-                the 8 TB/s HBM peak; traffic from committed rocprofv3 counter
-                summaries when they match the current kernel source, else null;
+                its mean event-to-event launch time, against the 8 TB/s HBM
+                peak; traffic from committed rocprofv3 counter summaries when
+                they match the current kernel source, else null;
   cpu_baseline  the fp64 oracle on the host cores over the same step;
   t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12.
 
@@ -77,13 +87,13 @@ class Stack:
         dev = "cuda"
         self.L = []
         ws_bytes = F.fsa_backward_workspace_size(B, H, T, D, F.FSA_DTYPE_BF16)
-        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         for l in range(layers):
             x = I.workload_inputs(wl, l)
             t = {n: I.to_device(x[n], wl.dtype) for n in ("q", "k", "v", "dout")}
             f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
             t.update(out=f32(B, H, T, D), lse=f32(B, H, T), dq=f32(B, H, T, D),
-                     dk=f32(B, H, T, D), dv=f32(B, H, T, D), dalpha=f32(1))
+                     dk=f32(B, H, T, D), dv=f32(B, H, T, D), dalpha=f32(1),
+                     ws=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev))
             self.L.append(t)
         self._prepare_calls(torch, F)
 
@@ -97,74 +107,102 @@ class Stack:
         B, H, T, D = wl.B, wl.H, wl.T, wl.D
         dt = F.FSA_DTYPE_BF16 if wl.dtype == "bf16" else F.FSA_DTYPE_F32
         stream = vp(torch.cuda.current_stream().cuda_stream)
-        ws, nws = vp(self.ws.data_ptr()), self.ws.numel()
-        self.calls = []
+        fwd, dq, dkdv = [], [], []
         for l, t in enumerate(self.L):
             p = {n: vp(x.data_ptr()) for n, x in t.items()}
+            nws = t["ws"].numel()
             a = f32(float(self.alphas[l]))
-            self.calls.append([
-                ("fwd", lib.fsa_forward, (p["q"], p["k"], p["v"], dt, B, H, T, D, a,
-                                          self.W, p["out"], p["lse"], stream)),
-                ("bwd_dq", lib.fsa_backward_dq, (p["q"], p["k"], p["v"], p["dout"],
+            fwd.append((lib.fsa_forward, (p["q"], p["k"], p["v"], dt, B, H, T, D, a,
+                                          self.W, p["out"], p["lse"], stream)))
+            dq.append((lib.fsa_backward_dq, (p["q"], p["k"], p["v"], p["dout"],
+                                             p["lse"], dt, B, H, T, D, a, self.W,
+                                             p["dq"], p["ws"], nws, stream)))
+            dkdv.append((lib.fsa_backward_dkdv, (p["q"], p["k"], p["v"], p["dout"],
                                                  p["lse"], dt, B, H, T, D, a, self.W,
-                                                 p["dq"], ws, nws, stream)),
-                ("bwd_dkdv", lib.fsa_backward_dkdv, (p["q"], p["k"], p["v"], p["dout"],
-                                                     p["lse"], dt, B, H, T, D, a,
-                                                     self.W, p["dk"], p["dv"],
-                                                     p["dalpha"], ws, nws, stream)),
-            ])
+                                                 p["dk"], p["dv"], p["dalpha"],
+                                                 p["ws"], nws, stream)))
+        # forward in layer order; backward in reverse layer order, dq stage then
+        # dk/dv stage of each layer
+        self.order = [("fwd",) + c for c in fwd]
+        for l in reversed(range(len(self.L))):
+            self.order += [("bwd_dq",) + dq[l], ("bwd_dkdv",) + dkdv[l]]
 
     def step(self, ev=None):
-        for layer_calls in self.calls:
-            for name, fn, args in layer_calls:
-                if ev is not None:
-                    ev.record(name)
-                st = fn(*args)
-                if st != 0:
-                    raise RuntimeError(f"{name} returned status {st}")
+        for name, fn, args in self.order:
             if ev is not None:
-                ev.record(None)
+                ev.record(name)
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError(f"{name} returned status {st}")
+        if ev is not None:
+            ev.record(None)
 
 
 class Events:
-    """Back-to-back HIP events on the launch stream; the time between the
-    event recorded before a launch and the next event is that launch's time.
-    All events are created up front, so recording one costs the host only the
-    enqueue."""
+    """Timing events on the launch stream, created through HIP with
+    hipEventDisableSystemFence (no cache writeback and invalidation at each
+    record). The time from the event before a launch to the next event is that
+    launch's time. All events are created up front, so recording one costs the
+    host only the enqueue."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, torch, count):
-        self.torch = torch
-        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")       # the runtime torch loaded
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.pool = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                                ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.pool.append(e)
         self.marks = []
-        self.stream = torch.cuda.current_stream()
 
     def record(self, name):
         e = self.pool[len(self.marks)]
-        e.record(self.stream)
+        if self.hip.hipEventRecord(e, self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
         self.marks.append((name, e))
 
     def per_kernel_ms(self):
         tot, cnt = {}, {}
+        f = self.ct.c_float()
         for (name, e0), (_, e1) in zip(self.marks, self.marks[1:]):
             if name is None:
                 continue
-            tot[name] = tot.get(name, 0.0) + e0.elapsed_time(e1)
+            if self.hip.hipEventElapsedTime(self.ct.byref(f), e0, e1) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            tot[name] = tot.get(name, 0.0) + f.value
             cnt[name] = cnt.get(name, 0) + 1
         return {n: tot[n] / cnt[n] for n in tot}, cnt
 
+    def close(self):
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
+        self.pool = []
+
 
 def time_stack(stack, steps, warmup, torch):
+    """Step time on the host clock with no events between launches; then the
+    per-kernel event times over as many steps again."""
     for _ in range(warmup):
         stack.step()
-    ev = Events(torch, steps * len(stack.calls) * (len(stack.calls[0]) + 1))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        stack.step(ev)
+        stack.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
+    ev = Events(torch, steps * (len(stack.order) + 1))
+    for _ in range(steps):
+        stack.step(ev)
+    torch.cuda.synchronize()
     per_ms, counts = ev.per_kernel_ms()
+    ev.close()
     return ms_step, per_ms, counts
 
 
