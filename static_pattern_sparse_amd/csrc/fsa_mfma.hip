@@ -635,6 +635,35 @@ __device__ __forceinline__ float tap_part(const f32x4& s, const LaneMasks& lm, f
   return wl * lo + wh * hi;
 }
 
+
+// Store a 16-row fp32 result tile held in the C layout of the products over
+// rows (lane (g, n): row n, columns 16mb + 4g .. +3) through LDS, so that each
+// non-temporal store instruction writes whole rows (1 KB: 4 rows at D = 64,
+// 2 at D = 128). Stored piecewise from the C layout, the non-temporal writes
+// cover half cache lines and are not merged (measured HBM writes 1.3-1.4x the
+// bytes). Row r of the tile goes to dst + r*D when row_ok(r); `buf` needs
+// 16 * (4D + 16) bytes and must no longer be read by this wavefront.
+template <int D, typename RowOk>
+__device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, float* dst, int lane,
+                                           RowOk row_ok) {
+  constexpr int kPitch = 4 * D + 16;                   // padded row (bank spread)
+  constexpr int kLanesPerRow = D / 4;                  // float4 per row
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb)
+    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(buf + n * kPitch + (16 * mb + 4 * g) * 4) = acc[mb];
+  __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int c = lane % kLanesPerRow;
+#pragma unroll
+  for (int it = 0; it < 16 / kRowsPerStore; ++it) {
+    const int r = kRowsPerStore * it + lane / kLanesPerRow;
+    const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(buf + r * kPitch + 16 * c);
+    if (row_ok(r)) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(dst + static_cast<size_t>(r) * D + 4 * c));
+  }
+}
+
 // ---------------------------------------------------------------- forward
 // One wavefront per 15-query tile. Key blocks are taken in pairs: the window
 // pairs first, then the tap pairs; K and V of a pair are staged in the
@@ -789,15 +818,15 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     __builtin_amdgcn_wave_barrier();
   }
 
-  if (qvalid) {
-    const float inv = 1.f / l;
-    float* o = out + base + static_cast<size_t>(i) * D + 4 * g;
+  const float inv = qvalid ? 1.f / l : 0.f;
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb)
-      st4_nt(o + 16 * mb, acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv);
-    if (g == 0)
-      __builtin_nontemporal_store((m + lg2(l)) * 0.6931471805599453f, lse + static_cast<size_t>(bh) * T + i);
-  }
+  for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[mb][j] *= inv;
+  store_tile<D>(lds, acc, out + base + static_cast<size_t>(i0) * D, lane,
+                [&](int r) { return r < kTileQ && i0 + r < T; });
+  if (qvalid && g == 0)
+    __builtin_nontemporal_store((m + lg2(l)) * 0.6931471805599453f, lse + static_cast<size_t>(bh) * T + i);
 }
 
 // ---------------------------------------------------------------- backward
@@ -967,15 +996,14 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   }
 
   const float Dl = rsum4(dwin) + dtap;
-  if (qvalid) {
-    float* o = dq + base + static_cast<size_t>(i) * D + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb)
-      st4_nt(o + 16 * mb, scale * (a1[mb][0] - Dl * a2[mb][0]), scale * (a1[mb][1] - Dl * a2[mb][1]),
-             scale * (a1[mb][2] - Dl * a2[mb][2]), scale * (a1[mb][3] - Dl * a2[mb][3]));
-    if (g == 0)
-      reinterpret_cast<float2*>(delta)[static_cast<size_t>(bh) * T + i] = make_float2(L2, Dl);
-  }
+  for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a1[mb][j] = scale * (a1[mb][j] - Dl * a2[mb][j]);
+  store_tile<D>(lds, a1, dq + base + static_cast<size_t>(i0) * D, lane,
+                [&](int r) { return r < kTileQ && i0 + r < T; });
+  if (qvalid && g == 0)
+    reinterpret_cast<float2*>(delta)[static_cast<size_t>(bh) * T + i] = make_float2(L2, Dl);
   float dal = al_a - Dl * (scale * al_b);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) dal += __shfl_xor(dal, off);
@@ -1196,20 +1224,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bw
     __builtin_amdgcn_wave_barrier();
   }
 
-  // output addresses formed here (an opaque copy of the lane index keeps the
-  // compiler from holding them in registers across the loops)
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  const int nn = ln & 15, gg = ln >> 4, rr = rowb + nn;
-  if (nn >= 1 && nn <= kTileK && rr < T) {
-    float* okp = dk + base + static_cast<size_t>(rr) * D + 4 * gg;
-    float* ovp = dv + base + static_cast<size_t>(rr) * D + 4 * gg;
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb) {
-      st4_nt(okp + 16 * mb, ak[mb][0] * scale, ak[mb][1] * scale, ak[mb][2] * scale, ak[mb][3] * scale);
-      st4_nt(ovp + 16 * mb, av[mb][0], av[mb][1], av[mb][2], av[mb][3]);
-    }
-  }
+  for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ak[mb][j] *= scale;
+  // rows 1 .. kTileK of the block are this tile's keys (0 and 15 are halos)
+  auto key_ok = [&](int r) { return r >= 1 && r <= kTileK && rowb + r < T; };
+  store_tile<D>(lds, ak, dk + base + static_cast<size_t>(rowb) * D, lane, key_ok);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  store_tile<D>(lds, av, dv + base + static_cast<size_t>(rowb) * D, lane, key_ok);
 }
 
 }  // namespace
