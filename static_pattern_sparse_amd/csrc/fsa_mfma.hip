@@ -13,25 +13,27 @@
 //   tap blocks     rows i0-c_k .. i0-c_k+15: query i0+n needs rows n and n+1 of
 //                  the block, which is why a tile holds 15 queries, not 16.
 // Scores of a block come from one 16x16 MFMA product S^T = K_block Q_tile^T
-// (v_mfma_f32_16x16x32_bf16, K rows as the A operand straight from global
-// memory, Q rows as the B operand held in registers). For a tap block only the
-// diagonal (weight 1-t) and the super-diagonal (weight t) of S^T are used.
+// (v_mfma_f32_16x16x32_bf16, K rows as the A operand read from the block
+// staged in LDS, Q rows as the B operand held in registers). For a tap block
+// only the diagonal (weight 1-t) and the super-diagonal (weight t) of S^T are
+// used.
 //
 // MFMA lane layout (16x16x32 bf16): lane l holds A[m=l%16][k=8(l/16)+e],
 // B[k=8(l/16)+e][n=l%16] and C[m=4(l/16)+j][n=l%16]. With n = l%16 the query of
 // the tile and g = l/16, lane (g, n) therefore holds the scores of query n
 // against block rows 4g..4g+3.
 //
-// The softmax is not online: a tile's whole attended set (at most
-// 16*nwb + 15 entries per query) fits in registers, so scores are formed
-// first, then max, sum and lse, then P.V.
+// Blocks are taken in pairs (window pairs, then tap pairs): K and V of a pair
+// are staged in the wavefront's LDS by coalesced direct-to-LDS loads, then
+// consumed. Softmax is online in log2 units (running max and sum per query).
 //
-// P.V is the product O^T = V_blk^T P^T over pairs of key blocks (32 MFMA
-// k-slots: slots 8g..8g+3 are rows 4g..4g+3 of block X, slots 8g+4..8g+7 rows
-// 4g..4g+3 of block Y), so the P values come straight from the score layout.
-// V^T is staged through LDS: each lane loads a 4x4 (row x column) bf16 patch,
-// transposes it with byte permutes and writes 4 keys per column. P is split
-// into bf16 hi + lo parts (two MFMAs) so its rounding stays near 2^-17.
+// P.V is the product O^T = V_blk^T P^T over the pair (32 MFMA k-slots: slots
+// 8g..8g+3 are rows 4g..4g+3 of block X, slots 8g+4..8g+7 rows 4g..4g+3 of
+// block Y), so the P values come straight from the score layout; V^T comes
+// from transposing LDS reads (ds_read_b64_tr_b16) of the staged block. P is
+// split into bf16 hi + lo parts (two MFMAs) so it keeps about 2^-16 relative.
+// The backward kernels below reuse the geometry (dq) or swap the roles of
+// queries and keys (dk/dv).
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -57,47 +59,6 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-__device__ __forceinline__ int clampi(int x, int lo, int hi) {
-  return x < lo ? lo : (x > hi ? hi : x);
-}
-
-__device__ __forceinline__ float xsum4(float x) {   // sum over g = 0..3
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-__device__ __forceinline__ float xmax4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-// bf16 hi/lo split of 8 fp32 values into two B operands.
-__device__ __forceinline__ void split_hi_lo(const float* p, u32x4* hi, u32x4* lo) {
-  bf16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 he = static_cast<__bf16>(p[e]);
-    h[e] = he;
-    l[e] = static_cast<__bf16>(p[e] - static_cast<float>(he));
-  }
-  *hi = __builtin_bit_cast(u32x4, h);
-  *lo = __builtin_bit_cast(u32x4, l);
-}
-
-// Order the LDS accesses of one wavefront (its lanes exchange data through
-// LDS; LDS requests of a wavefront complete in order).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Map the 1-D workgroup id to (head, tile). Workgroups are dispatched
 // round-robin over the 8 XCDs; when the head count allows, all tiles of one
 // head go to one XCD, consecutively, so the rows its taps re-read stay in
@@ -118,68 +79,6 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int n_tiles, int* bh,
   }
 }
 
-// S^T block (16 rows from row0) x Q tile: lane (g, n) gets q_n . K[row0+4g+j].
-template <int D>
-__device__ __forceinline__ f32x4 score_block(const uint16_t* K, int row0, int T,
-                                             const u32x4* qb, int n, int g) {
-  const int row = clampi(row0 + n, 0, T - 1);
-  const uint16_t* p = K + static_cast<size_t>(row) * D + 8 * g;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) acc = mfma(ld16(p + 32 * s), qb[s], acc);
-  return acc;
-}
-
-// Stage rows row0..row0+15 of X (clamped to the sequence) transposed into the
-// X (half = 0) or Y (half = 1) half of an LDS pair buffer; lane (cc, rg)
-// handles rows 4rg..4rg+3 and columns 4cc..4cc+3 (+64h). A missing block
-// (row0 == INT_MIN) is written as zeros.
-template <int D>
-__device__ __forceinline__ void stage_t(const uint16_t* X, int row0, int T,
-                                         char* lds, int half, int lane) {
-  const int cc = lane >> 2, rg = lane & 3;
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {
-    uint2 r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (row0 == INT_MIN) {
-        r[i] = make_uint2(0u, 0u);
-      } else {
-        const int row = clampi(row0 + 4 * rg + i, 0, T - 1);
-        r[i] = *reinterpret_cast<const uint2*>(X + static_cast<size_t>(row) * D +
-                                               64 * h + 4 * cc);
-      }
-    }
-    const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
-    uint2 col[4];
-    col[0] = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel_lo),
-                        __builtin_amdgcn_perm(r[3].x, r[2].x, sel_lo));
-    col[1] = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, sel_hi),
-                        __builtin_amdgcn_perm(r[3].x, r[2].x, sel_hi));
-    col[2] = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel_lo),
-                        __builtin_amdgcn_perm(r[3].y, r[2].y, sel_lo));
-    col[3] = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, sel_hi),
-                        __builtin_amdgcn_perm(r[3].y, r[2].y, sel_hi));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d = 64 * h + 4 * cc + c;
-      *reinterpret_cast<uint2*>(lds + d * kLdsRowBytes + 32 * half + 8 * rg) = col[c];
-    }
-  }
-}
-
-// A operand X^T of a product over rows (d-block mb): lane (g, n) reads
-// d = 16mb + n, rows 4g..4g+3 of block X and of block Y.
-__device__ __forceinline__ u32x4 t_operand(const char* lds, int mb, int n, int g) {
-  const char* row = lds + (16 * mb + n) * kLdsRowBytes + 8 * g;
-  const uint2 x = *reinterpret_cast<const uint2*>(row);
-  const uint2 y = *reinterpret_cast<const uint2*>(row + 32);
-  u32x4 a;
-  a[0] = x.x; a[1] = x.y; a[2] = y.x; a[3] = y.y;
-  return a;
-}
-
 // ---------------------------------------------------------------- buffer access
 // Every (b, h) slab is read through a buffer resource that covers exactly the
 // slab (T*D bf16). Offsets outside it -- rows before 0 or at or past T -- read
@@ -198,20 +97,10 @@ struct Slab {
   uint32_t bytes;
 };
 
-__device__ __forceinline__ u32x4 bld16(rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // Streaming (non-temporal) variant for rows read once per launch, so that
 // they do not displace the rows the taps re-read from L2.
 __device__ __forceinline__ u32x4 bld16_nt(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
-}
-
-// Non-temporal stores of the fp32 results (written once, never re-read by
-// the launch).
-__device__ __forceinline__ void st4_nt(float* p, float a, float b, float c, float d) {
-  __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
 }
 
 // Keep a byte offset whole in the VGPR operand: a constant part folded into
@@ -295,70 +184,36 @@ __device__ __forceinline__ f32x4 mfma_rows(const u32x4* a, const u32x4* b) {
   return acc;
 }
 
-// The 4x4 patches of V (or any row tensor) that lane (cc, rg) stages for a
-// 16-row block: rows row0 + 4rg + i, columns 4cc..4cc+3 (+64h).
-// `lane_v` = 4rg*2D + 8cc.
-template <int D>
-__device__ __forceinline__ void bload_patch(rsrc_t r, int lane_v, int row0, uint2 (*p)[4]) {
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[h][i] = bld8(r, lane_v + (row0 + i) * (2 * D) + 128 * h);
+// Register j of a C fragment, j = 2*b1 + b0 given as lane-constant selects.
+__device__ __forceinline__ float pick4(const f32x4& x, bool b0, bool b1) {
+  const float lo = b0 ? x[1] : x[0];
+  const float hi = b0 ? x[3] : x[2];
+  return b1 ? hi : lo;
 }
 
-// Transpose the patch in registers and write it into half `half` of an LDS
-// pair buffer laid out [d][32 rows] with kLdsRowBytes per d.
-// `lane_w` = 4cc*kLdsRowBytes + 8rg.
-template <int D>
-__device__ __forceinline__ void write_patch(char* lds, int lane_w, int half,
-                                            const uint2 (*p)[4]) {
-  const uint32_t lo = 0x05040100u, hi = 0x07060302u;
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {
-    const uint2* r = p[h];
-    char* w = lds + lane_w + 32 * half + h * 64 * kLdsRowBytes;
-    *reinterpret_cast<uint2*>(w) = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, lo),
-                                              __builtin_amdgcn_perm(r[3].x, r[2].x, lo));
-    *reinterpret_cast<uint2*>(w + kLdsRowBytes) = make_uint2(__builtin_amdgcn_perm(r[1].x, r[0].x, hi),
-                                                             __builtin_amdgcn_perm(r[3].x, r[2].x, hi));
-    *reinterpret_cast<uint2*>(w + 2 * kLdsRowBytes) = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, lo),
-                                                                 __builtin_amdgcn_perm(r[3].y, r[2].y, lo));
-    *reinterpret_cast<uint2*>(w + 3 * kLdsRowBytes) = make_uint2(__builtin_amdgcn_perm(r[1].y, r[0].y, hi),
-                                                                 __builtin_amdgcn_perm(r[3].y, r[2].y, hi));
-  }
-}
-
-__device__ __forceinline__ void zero_patch(uint2 (*p)[4], int nh) {
-  for (int h = 0; h < nh; ++h)
-    for (int i = 0; i < 4; ++i) p[h][i] = make_uint2(0u, 0u);
-}
-
-// A operand X^T of a product over rows, d-block mb: lane (g, n) reads d-row
-// 16mb + n, rows 4g..4g+3 of block X and of block Y. `lane_t` = n*kLdsRowBytes + 8g.
-__device__ __forceinline__ u32x4 lds_operand(const char* lds, int lane_t, int mb) {
-  const char* row = lds + lane_t + mb * 16 * kLdsRowBytes;
-  const uint2 x = *reinterpret_cast<const uint2*>(row);
-  const uint2 y = *reinterpret_cast<const uint2*>(row + 32);
-  u32x4 a;
-  a[0] = x.x; a[1] = x.y; a[2] = y.x; a[3] = y.y;
-  return a;
-}
-
-// Per-lane constants of the 16x16 C layout: lane (g, n) holds rows 4g..4g+3 of
+// Per-lane selects of the 16x16 C layout: lane (g, n) holds rows 4g..4g+3 of
 // column n. For a tap block, query column n takes row n with weight 1-t and
-// row n+1 with weight t; mlo/mhi mark which of the lane's 4 rows those are.
-struct LaneMasks {
-  float mlo[4], mhi[4];
+// row n+1 with weight t; the selects pick which of the lane's 4 rows those
+// are (lane-constant booleans live in scalar mask registers, not VGPRs).
+struct LaneSel {
+  bool on_lo, lo0, lo1;    // register n - 4g, if it is one of this lane's
+  bool on_hi, hi0, hi1;    // register n + 1 - 4g, likewise
 };
 
-__device__ __forceinline__ LaneMasks lane_masks(int n, int g) {
-  LaneMasks m;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m.mlo[j] = (4 * g + j == n) ? 1.f : 0.f;
-    m.mhi[j] = (4 * g + j == n + 1) ? 1.f : 0.f;
-  }
-  return m;
+__device__ __forceinline__ LaneSel lane_sel(int n, int g) {
+  const int jl = n - 4 * g, jh = n + 1 - 4 * g;
+  return LaneSel{jl >= 0 && jl < 4, (jl & 1) != 0, (jl & 2) != 0,
+                 jh >= 0 && jh < 4, (jh & 1) != 0, (jh & 2) != 0};
+}
+
+// The lower-row (row n) and upper-row (row n + 1) terms of a tap block's
+// scores held by lane (g, n), zero where the lane holds neither; the
+// cross-row sum over g completes them.
+__device__ __forceinline__ float pick_lo(const f32x4& s, const LaneSel& ls) {
+  return ls.on_lo ? pick4(s, ls.lo0, ls.lo1) : 0.f;
+}
+__device__ __forceinline__ float pick_hi(const f32x4& s, const LaneSel& ls) {
+  return ls.on_hi ? pick4(s, ls.hi0, ls.hi1) : 0.f;
 }
 
 // ---------------------------------------------------------------- LDS tiles
@@ -469,19 +324,6 @@ __device__ __forceinline__ void stage_two(Slab ra, Slab rb, const TileLane<D>& t
     stage_block<D>(ra, tl, r1, st + kB);
     stage_block<D>(rb, tl, r1, st + 3 * kB);
   }
-}
-
-// First row of block hf of pair p: `nwp` pairs of 16-row blocks
-// base0 + step*b (b < nb) come first, then pairs of taps at base1 + sgn*c_t.
-__device__ __forceinline__ int pair_row(int p, int hf, int nwp, int nb, int base0,
-                                        int step, int ntap, int base1, int sgn,
-                                        const Taps& taps) {
-  if (p < nwp) {
-    const int b = 2 * p + hf;
-    return b < nb ? base0 + step * b : INT_MIN;
-  }
-  const int t = 2 * (p - nwp) + hf;
-  return t < ntap ? base1 + sgn * taps.c[t] : INT_MIN;
 }
 
 template <int D>
@@ -623,16 +465,10 @@ __device__ __forceinline__ void tap_operands(float ax, float bx, float ay, float
   (*lo)[3] = __builtin_amdgcn_perm(rby, ray, ts.s23);
 }
 
-// Masked parts of a tap block's scores in lane (g, n): the lower-row term
-// (row n) and the upper-row term (row n + 1); the cross-row sum completes them.
-__device__ __forceinline__ float tap_part(const f32x4& s, const LaneMasks& lm, float wl, float wh) {
-  float lo = 0.f, hi = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lo = fmaf(lm.mlo[j], s[j], lo);
-    hi = fmaf(lm.mhi[j], s[j], hi);
-  }
-  return wl * lo + wh * hi;
+// Weighted tap score part of lane (g, n): (1-t) x lower-row term + t x
+// upper-row term.
+__device__ __forceinline__ float tap_part(const f32x4& s, const LaneSel& ls, float wl, float wh) {
+  return wl * pick_lo(s, ls) + wh * pick_hi(s, ls);
 }
 
 
@@ -703,7 +539,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
   const float c2 = pr.scale * kLog2e;                 // scores in log2 units
-  const LaneMasks lm = lane_masks(n, g);
+  const LaneSel ls = lane_sel(n, g);
   const int nwb = (W + kTileQ - 1) / 16 + 1;
   const int nwp = (nwb + 1) / 2;
   const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
@@ -789,7 +625,7 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     const f32x4 s0 = mfma_rows<D>(ka, qb);
     nat_operand<D>(lds + Tl::kBlockBytes, tl, ka);
     const f32x4 s1 = mfma_rows<D>(ka, qb);
-    float x0 = tap_part(s0, lm, wl0, wh0), x1 = tap_part(s1, lm, wl1, wh1);
+    float x0 = tap_part(s0, ls, wl0, wh0), x1 = tap_part(s1, ls, wl1, wh1);
     rsum4x2(&x0, &x1);
     const float sc0 = (qvalid && i >= c0) ? x0 * c2 : -INFINITY;
     const float sc1 = (qvalid && has1 && i >= c1) ? x1 * c2 : -INFINITY;
@@ -874,7 +710,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const float scale = pr.scale;
   const float c2 = scale * kLog2e;
   const float L2 = qvalid ? lse[static_cast<size_t>(bh) * T + i] * kLog2e : 0.f;
-  const LaneMasks lm = lane_masks(n, g);
+  const LaneSel ls = lane_sel(n, g);
   const int nwb = (W + kTileQ - 1) / 16 + 1;
   const int nwp = (nwb + 1) / 2;
   const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
@@ -940,9 +776,6 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   // lane (g, n)); they are linear in those parts, so the final sum over all
   // lanes completes them without a cross-row sum per entry.
   const TapSel ts = tap_sel(n, g);
-  float dm[4];                                          // mhi - mlo
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dm[j] = lm.mhi[j] - lm.mlo[j];
   for (int tp = 0; 2 * tp < ntap; ++tp) {
     const int t0 = 2 * tp, t1 = t0 + 1;
     const bool has1 = t1 < ntap;
@@ -953,25 +786,27 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     stage_two<D>(sk, sv, tl, i0 - c0, has1 ? i0 - c1 : INT_MIN, lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    u32x4 ka[D / 32];
-    nat_operand<D>(lds, tl, ka);
-    const f32x4 s0 = mfma_rows<D>(ka, qb);
-    nat_operand<D>(lds + Tl::kBlockBytes, tl, ka);
-    const f32x4 s1 = mfma_rows<D>(ka, qb);
-    nat_operand<D>(lds + 2 * Tl::kBlockBytes, tl, ka);
-    const f32x4 d0 = mfma_rows<D>(ka, gb);
-    nat_operand<D>(lds + 3 * Tl::kBlockBytes, tl, ka);
-    const f32x4 d1 = mfma_rows<D>(ka, gb);
-    float ps0 = tap_part(s0, lm, wl0, wh0), ps1 = tap_part(s1, lm, wl1, wh1);
-    float pd0 = tap_part(d0, lm, wl0, wh0), pd1 = tap_part(d1, lm, wl1, wh1);
-    float sdf0 = 0.f, sdf1 = 0.f, gdf0 = 0.f, gdf1 = 0.f;
+    // one block at a time: its score fragments reduce to the lane's two
+    // picks before the next block's are formed
+    float sl[2], sh[2], dl[2], dh[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sdf0 = fmaf(dm[j], s0[j], sdf0);
-      sdf1 = fmaf(dm[j], s1[j], sdf1);
-      gdf0 = fmaf(dm[j], d0[j], gdf0);
-      gdf1 = fmaf(dm[j], d1[j], gdf1);
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4 ka[D / 32];
+      nat_operand<D>(lds + hf * Tl::kBlockBytes, tl, ka);
+      const f32x4 sx = mfma_rows<D>(ka, qb);
+      nat_operand<D>(lds + (2 + hf) * Tl::kBlockBytes, tl, ka);
+      const f32x4 dx = mfma_rows<D>(ka, gb);
+      sl[hf] = pick_lo(sx, ls);
+      sh[hf] = pick_hi(sx, ls);
+      dl[hf] = pick_lo(dx, ls);
+      dh[hf] = pick_hi(dx, ls);
     }
+    const float sl0 = sl[0], sh0 = sh[0], sl1 = sl[1], sh1 = sh[1];
+    const float dl0 = dl[0], dh0 = dh[0], dl1 = dl[1], dh1 = dh[1];
+    float ps0 = wl0 * sl0 + wh0 * sh0, ps1 = wl1 * sl1 + wh1 * sh1;
+    float pd0 = wl0 * dl0 + wh0 * dh0, pd1 = wl1 * dl1 + wh1 * dh1;
+    const float sdf0 = sh0 - sl0, sdf1 = sh1 - sl1;     // per-lane parts of q.(K[a+1]-K[a])
+    const float gdf0 = dh0 - dl0, gdf1 = dh1 - dl1;     // and of dout.(V[a+1]-V[a])
     rsum4x2(&ps0, &ps1);
     rsum4x2(&pd0, &pd1);
     const float pe0 = (qvalid && i >= c0) ? ex2(ps0 * c2 - L2) : 0.f;
@@ -979,17 +814,22 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     dtap += pe0 * pd0 + pe1 * pd1;
     al_a += nf0 * pe0 * (pd0 * scale * sdf0 + gdf0) + nf1 * pe1 * (pd1 * scale * sdf1 + gdf1);
     al_b += nf0 * pe0 * sdf0 + nf1 * pe1 * sdf1;
-    u32x4 h1, l1, h2, l2;
+    // K^T (P o dP) first, then K^T P: one pair of hi/lo operands live at a time
+    u32x4 ohi, olo;
     const float q0 = pe0 * pd0, q1 = pe1 * pd1;
-    tap_operands(q0 * wl0, q0 * wh0, q1 * wl1, q1 * wh1, ts, &h1, &l1);
-    tap_operands(pe0 * wl0, pe0 * wh0, pe1 * wl1, pe1 * wh1, ts, &h2, &l2);
+    tap_operands(q0 * wl0, q0 * wh0, q1 * wl1, q1 * wh1, ts, &ohi, &olo);
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) {
       const u32x4 a = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
-      a1[mb] = mfma(a, h1, a1[mb]);
-      a1[mb] = mfma(a, l1, a1[mb]);
-      a2[mb] = mfma(a, h2, a2[mb]);
-      a2[mb] = mfma(a, l2, a2[mb]);
+      a1[mb] = mfma(a, ohi, a1[mb]);
+      a1[mb] = mfma(a, olo, a1[mb]);
+    }
+    tap_operands(pe0 * wl0, pe0 * wh0, pe1 * wl1, pe1 * wh1, ts, &ohi, &olo);
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      const u32x4 a = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
+      a2[mb] = mfma(a, ohi, a2[mb]);
+      a2[mb] = mfma(a, olo, a2[mb]);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
@@ -1018,7 +858,9 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 //           r + c - 1 (r is then the upper interpolation row).
 // The query rows involved come in 16-row query blocks: window blocks
 // rowb + 16b, and for a tap the 15 queries ib = j0+c-1 .. ib+14, which use
-// block rows n' and n'+1 (the forward's geometry with the roles swapped).
+// block rows n' and n'+1 (the forward's geometry with the roles swapped). A
+// 15-key tile would need query ib+15, whose upper row is the next tile's
+// first key: its score is not in this block's product.
 // Query and dout blocks of a pair are staged in LDS;
 // scores are recomputed as S = Q_blk K^T (query rows natural from LDS as A,
 // the tile's key rows as B in registers), so lane (g, m) holds query 4g+j
@@ -1027,13 +869,6 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
 // upper-row score register jj of lane m + 1 (one row shift).
 // dk^T += Q_blk^T (W o dS) and dv^T += dout_blk^T (W o P) read Q^T and dout^T
 // transposed from the same LDS tiles.
-
-// Select register j of a C fragment, j = 2*b1 + b0 given as lane masks.
-__device__ __forceinline__ float pick4(const f32x4& x, bool b0, bool b1) {
-  const float lo = b0 ? x[1] : x[0];
-  const float hi = b0 ? x[3] : x[2];
-  return b1 ? hi : lo;
-}
 
 // P operand selectors of a key-side tap block: lane (g, m) places its own
 // query's weight a at slot jj = m - 4g and the previous lane's weight b (query
