@@ -3,7 +3,8 @@
 Only the tests, the package smoke check and the benchmark's CPU-baseline leg
 may import this package. It shares no code with the HIP library.
 """
-from .fsa_oracle import (FIB, SCHEDULE_COPRIME, SCHEDULE_FIXED,  # noqa: F401
+from .fsa_oracle import (BASES, FIB, MODES, POW2, SCHEDULE_COPRIME,  # noqa: F401
+                         SCHEDULE_FIXED, TapTable,
                          SCHEDULE_LINEAR, backward, backward_slab, dkdv_rows,
                          dq_rows, forward, forward_rows, forward_slab,
                          offset_table, schedule)

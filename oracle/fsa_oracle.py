@@ -39,6 +39,16 @@ Readings taken where the page leaves a step open:
 * R8 d(alpha) at an integer d_k uses the right-hand slope K[a+1] - K[a].
 * R9 the schedule for L layers: linear alpha_l = a_min + (a_max-a_min)*l/(L-1)
   evaluated in fp64 and rounded once to fp32; coprime out[(s*l) mod L] = lin[l].
+* R10 the power-of-two control base (Methodology > Control variables) is the
+  fifteen terms 1, 2, 4, ..., 16384: the page's examples of offsets first met at
+  4096 tokens (1024, 2048; Core contributions and results > 3. Length
+  extrapolation, base sensitivity) need a ladder past 987, and fifteen terms
+  match the Fibonacci list's count.
+* R11 the rounded (mask) mode of the static runs (Core contributions and
+  results > 2. Learned dilation is inert, efficiency) attends row i - round(d_k)
+  with round to nearest, ties to even; a term is kept under the same rule
+  d_k >= W and applies to query i when i >= round(d_k). The attended rows do
+  not depend on alpha there, so d(loss)/d(alpha) = 0.
 
 Every array argument is float64 (the caller up-casts the dtype-rounded inputs
 exactly). Shapes are [B, H, T, D] (or a single [T, D] slab for the *_slab
@@ -48,12 +58,29 @@ helpers).
 from __future__ import annotations
 
 import math
+from typing import NamedTuple
 
 import numpy as np
 
 # [DSFS: Methodology > Architecture and attention > Attended set] -- the fifteen
 # Fibonacci distances, 1 through 987, the leading 1 taken once.
 FIB = (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987)
+
+# [DSFS: Methodology > Control variables] -- the power-of-two base, reading R10.
+POW2 = tuple(2 ** n for n in range(15))
+
+BASES = {"fib": FIB, "pow2": POW2}
+MODES = ("lerp", "round")
+
+
+class TapTable(NamedTuple):
+    """Per base term k: distance d, lower-row distance c, upper-row weight t,
+    kept flag, and the slope d(sample position)/d(alpha) of the term."""
+    d: np.ndarray
+    c: np.ndarray
+    t: np.ndarray
+    keep: np.ndarray
+    slope: np.ndarray
 
 SCHEDULE_FIXED = 0
 SCHEDULE_LINEAR = 1
@@ -98,23 +125,36 @@ def schedule(kind: int, num_layers: int = 16, a_min: float = 0.5,
 # ---------------------------------------------------------------------------
 # offset table  [DSFS: Methodology > Architecture and attention > Scaling]
 # ---------------------------------------------------------------------------
-def offset_table(alpha: float, window: int, round_alpha_to_fp32: bool = True):
-    """Return (d, c, t, keep) for the fifteen Fibonacci taps.
+def offset_table(alpha: float, window: int, round_alpha_to_fp32: bool = True,
+                 base: str = "fib", mode: str = "lerp") -> TapTable:
+    """Return the TapTable of the fifteen base terms.
 
     d_k = alpha*f_k (exact in fp64 when alpha is an fp32 value, reading R7),
-    c_k = ceil(d_k) (distance to the lower interpolation row, reading R4),
-    t_k = c_k - d_k in [0, 1) (weight of the upper row, reading R4),
-    keep_k = d_k >= W (reading R2).
+    keep_k = d_k >= W (reading R2), and
+      lerp:  c_k = ceil(d_k) (distance to the lower interpolation row),
+             t_k = c_k - d_k in [0, 1) (weight of the upper row, reading R4),
+             slope_k = -f_k (the sample position i - alpha*f_k moves with alpha);
+      round: c_k = round(d_k), ties to even, t_k = 0, slope_k = 0 (reading R11).
 
     `round_alpha_to_fp32=False` keeps alpha in fp64; only finite-difference
     tests use it, to step alpha by less than an fp32 ulp.
     """
+    if base not in BASES or mode not in MODES:
+        raise ValueError("unknown base or mode")
     a = float(np.float32(alpha)) if round_alpha_to_fp32 else float(alpha)
-    d = np.array([a * f for f in FIB], dtype=np.float64)
-    c = np.ceil(d).astype(np.int64)
-    t = c.astype(np.float64) - d
+    f = np.array(BASES[base], dtype=np.float64)
+    d = a * f
+    if mode == "lerp":
+        c = np.ceil(d).astype(np.int64)
+        t = c.astype(np.float64) - d
+        slope = -f
+    else:
+        # Python's round() on a float is round-half-even and exact
+        c = np.array([round(float(x)) for x in d], dtype=np.int64)
+        t = np.zeros_like(d)
+        slope = np.zeros_like(d)
     keep = d >= float(window)
-    return d, c, t, keep
+    return TapTable(d, c, t, keep, slope)
 
 
 # ---------------------------------------------------------------------------
@@ -124,16 +164,16 @@ def _entries(T: int, window: int, table):
     """List the attended entries as (kind, info) records.
 
     ("win", w): window entry at key j = i - w, valid for i >= w (reading R1).
-    ("tap", k, c_k, t_k): tap entry with lower row a = i - c_k and upper row
-    a + 1, valid for i >= c_k (reading R3).
+    ("tap", k, c_k, t_k, slope_k): tap entry with lower row a = i - c_k and
+    upper row a + 1, valid for i >= c_k (reading R3).
     """
-    d, c, t, keep = table
     ents = []
     for w in range(min(window, T)):
         ents.append(("win", w))
-    for k in range(len(FIB)):
-        if keep[k] and c[k] <= T - 1:
-            ents.append(("tap", k, int(c[k]), float(t[k])))
+    for k in range(len(table.c)):
+        if table.keep[k] and table.c[k] <= T - 1:
+            ents.append(("tap", k, int(table.c[k]), float(table.t[k]),
+                         float(table.slope[k])))
     return ents
 
 
@@ -142,7 +182,7 @@ def _entry_rows(e, T):
     if e[0] == "win":
         w = e[1]
         return w, w, 1.0, 0.0
-    _, k, ck, tk = e
+    ck, tk = e[2], e[3]
     return ck, ck, 1.0 - tk, tk
 
 
@@ -171,7 +211,7 @@ def _scores_slab(q, k, ents, scale):
     return S
 
 
-def forward_slab(q, k, v, alpha, window, table=None):
+def forward_slab(q, k, v, alpha, window, table=None, base="fib", mode="lerp"):
     """Forward pass on one [T, D] slab; returns (out[T, D], lse[T]).
 
     One softmax over the union of window and tap entries (reading R5), scaled by
@@ -181,7 +221,7 @@ def forward_slab(q, k, v, alpha, window, table=None):
     """
     T, D = q.shape
     if table is None:
-        table = offset_table(alpha, window)
+        table = offset_table(alpha, window, base=base, mode=mode)
     scale = 1.0 / math.sqrt(D)
     ents = _entries(T, window, table)
     S = _scores_slab(q, k, ents, scale)
@@ -196,7 +236,8 @@ def forward_slab(q, k, v, alpha, window, table=None):
     return out, lse
 
 
-def backward_slab(q, k, v, dout, alpha, window, table=None):
+def backward_slab(q, k, v, dout, alpha, window, table=None, base="fib",
+                  mode="lerp"):
     """Backward pass on one slab; returns (dq, dk, dv, dalpha, lse).
 
     With p and the entry values from the forward definition:
@@ -206,15 +247,17 @@ def backward_slab(q, k, v, dout, alpha, window, table=None):
     and each entry hands its key/value gradient back to the rows it was
     gathered from, with the interpolation weights (1 - t) on the lower row and t
     on the upper row. Moving alpha moves the sample position i - alpha*f_k, so
-      dalpha = sum over taps and queries of -f_k * [ scale*dS * q_i.(K[a+1]-K[a])
-                                                     + p * dout_i.(V[a+1]-V[a]) ]
+      dalpha = sum over taps and queries of slope_k * [ scale*dS * q_i.(K[a+1]-K[a])
+                                                        + p * dout_i.(V[a+1]-V[a]) ]
+    with slope_k = -f_k when the distance interpolates and 0 in the rounded
+    mode (reading R11)
     [DSFS: Methodology > Architecture and attention > Implementation (gradient
     to alpha); Experimental variables > Learned]. Reading R8 fixes the slope at
     integer distances.
     """
     T, D = q.shape
     if table is None:
-        table = offset_table(alpha, window)
+        table = offset_table(alpha, window, base=base, mode=mode)
     scale = 1.0 / math.sqrt(D)
     ents = _entries(T, window, table)
     S = _scores_slab(q, k, ents, scale)
@@ -246,12 +289,13 @@ def backward_slab(q, k, v, dout, alpha, window, table=None):
         if e[0] == "tap":
             dk[i0 - off + 1: T - off + 1] += w_hi * scale * gs * q[i0:]
             dv[i0 - off + 1: T - off + 1] += w_hi * gp * dout[i0:]
-            f = FIB[e[1]]
-            dK = k[i0 - off + 1: T - off + 1] - k[i0 - off: T - off]
-            dV = v[i0 - off + 1: T - off + 1] - v[i0 - off: T - off]
-            term = (scale * dS[i0:, n] * np.einsum("td,td->t", q[i0:], dK)
-                    + P[i0:, n] * np.einsum("td,td->t", dout[i0:], dV))
-            dalpha += -f * float(term.sum())
+            slope = e[4]
+            if slope != 0.0:
+                dK = k[i0 - off + 1: T - off + 1] - k[i0 - off: T - off]
+                dV = v[i0 - off + 1: T - off + 1] - v[i0 - off: T - off]
+                term = (scale * dS[i0:, n] * np.einsum("td,td->t", q[i0:], dK)
+                        + P[i0:, n] * np.einsum("td,td->t", dout[i0:], dV))
+                dalpha += slope * float(term.sum())
     dq *= scale
     return dq, dk, dv, dalpha, lse
 
@@ -259,10 +303,10 @@ def backward_slab(q, k, v, dout, alpha, window, table=None):
 # ---------------------------------------------------------------------------
 # batched entry points over [B, H, T, D]
 # ---------------------------------------------------------------------------
-def forward(q, k, v, alpha, window):
+def forward(q, k, v, alpha, window, base="fib", mode="lerp"):
     """Forward over [B, H, T, D] fp64 arrays; returns (out, lse)."""
     B, H, T, D = q.shape
-    table = offset_table(alpha, window)
+    table = offset_table(alpha, window, base=base, mode=mode)
     out = np.empty_like(q)
     lse = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
@@ -272,11 +316,11 @@ def forward(q, k, v, alpha, window):
     return out, lse
 
 
-def backward(q, k, v, dout, alpha, window):
+def backward(q, k, v, dout, alpha, window, base="fib", mode="lerp"):
     """Backward over [B, H, T, D]; returns (dq, dk, dv, dalpha) with dalpha
     summed over every batch entry, head and position."""
     B, H, T, D = q.shape
-    table = offset_table(alpha, window)
+    table = offset_table(alpha, window, base=base, mode=mode)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
@@ -293,10 +337,10 @@ def backward(q, k, v, dout, alpha, window):
 # ---------------------------------------------------------------------------
 # single rows, for spot checks at sizes where whole slabs are too costly
 # ---------------------------------------------------------------------------
-def forward_rows(q, k, v, alpha, window, rows):
+def forward_rows(q, k, v, alpha, window, rows, base="fib", mode="lerp"):
     """out[i], lse[i] of one slab for the listed query rows only."""
     T, D = q.shape
-    table = offset_table(alpha, window)
+    table = offset_table(alpha, window, base=base, mode=mode)
     scale = 1.0 / math.sqrt(D)
     ents = _entries(T, window, table)
     outs, lses = [], []
@@ -328,10 +372,10 @@ def _row_entries(q, k, v, ents, i, scale):
     return s_list, v_list
 
 
-def dq_rows(q, k, v, dout, alpha, window, rows):
+def dq_rows(q, k, v, dout, alpha, window, rows, base="fib", mode="lerp"):
     """dq[i] and Delta_i of one slab for the listed query rows only."""
     T, D = q.shape
-    table = offset_table(alpha, window)
+    table = offset_table(alpha, window, base=base, mode=mode)
     scale = 1.0 / math.sqrt(D)
     ents = _entries(T, window, table)
     res, deltas = [], []
@@ -356,11 +400,11 @@ def dq_rows(q, k, v, dout, alpha, window, rows):
     return np.array(res), np.array(deltas)
 
 
-def dkdv_rows(q, k, v, dout, alpha, window, rows):
+def dkdv_rows(q, k, v, dout, alpha, window, rows, base="fib", mode="lerp"):
     """dk[j], dv[j] of one slab for the listed key rows only, by enumerating
     every (query, entry) pair that gathers row j."""
     T, D = q.shape
-    table = offset_table(alpha, window)
+    table = offset_table(alpha, window, base=base, mode=mode)
     scale = 1.0 / math.sqrt(D)
     ents = _entries(T, window, table)
     cache = {}

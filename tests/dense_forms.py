@@ -22,6 +22,8 @@ import math
 import torch
 
 FIB_LIST = [1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987]
+# power-of-two control base [same page: Methodology > Control variables]
+POW2_LIST = [1 << n for n in range(15)]
 
 
 def attended_sets(T, window, distances):
@@ -50,7 +52,7 @@ def dense_masked(q, k, v, sets):
     return P @ v, lse
 
 
-def matrix_form(q, k, v, alpha, window):
+def matrix_form(q, k, v, alpha, window, base_list=FIB_LIST):
     """Sparse attention through explicit interpolation matrices.
 
     alpha: 0-dim float64 torch tensor (may require grad). Distances d = alpha*f
@@ -63,7 +65,7 @@ def matrix_form(q, k, v, alpha, window):
     win_mask = (idx[None, :] <= idx[:, None]) & (idx[None, :] > idx[:, None] - window)
     Sw = (scale * (q @ k.T)).masked_fill(~win_mask, float("-inf"))
     tap_s, tap_v = [], []
-    for f in FIB_LIST:
+    for f in base_list:
         d = alpha * f
         dval = float(d.detach())
         if dval < window:

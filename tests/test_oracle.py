@@ -80,20 +80,21 @@ def test_schedule_rejects_bad_args():
 # ---------------------------------------------------------------- offsets
 @pytest.mark.parametrize("alpha", [1.0, 0.5, 1.5, 0.7317, 1.2913])
 def test_offset_table_exact(alpha):
-    d, c, t, keep = O.offset_table(alpha, 12)
+    d, c, t, keep, slope = O.offset_table(alpha, 12)
     a = Fraction(float(np.float32(alpha)))
     for n, f in enumerate(O.FIB):
         assert Fraction(float(d[n])) == a * f          # exact product
         assert Fraction(int(c[n])) - Fraction(float(t[n])) == a * f
         assert 0.0 <= t[n] < 1.0
         assert keep[n] == (a * f >= 12)
+        assert slope[n] == -f                          # position i - alpha*f
 
 
 def test_offset_table_stagger_near_integer():
     # fp32(0.5 + 5/15) * 144 sits just below 120: the distance is fractional,
     # the lower row is i - 120 and the upper row i - 119 gets a tiny weight
     a = O.schedule(O.SCHEDULE_LINEAR, 16)[5]
-    d, c, t, keep = O.offset_table(a, 12)
+    d, c, t, keep, _ = O.offset_table(a, 12)
     n = O.FIB.index(144)
     assert c[n] == 120 and 0.0 < t[n] < 1e-5
 
@@ -336,6 +337,6 @@ def test_pins_catch_wrong_dalpha_sign(monkeypatch):
     fd = (_loss(q, k, v, g, alpha + h, W) - _loss(q, k, v, g, alpha - h, W)) / (2 * h)
     # plant a sign error in the dalpha accumulation only (the table keeps the
     # true distances): the finite-difference pin must reject it
-    monkeypatch.setattr(O, "FIB", tuple(-f for f in O.FIB))
-    _, _, _, da_bad, _ = O.backward_slab(q, k, v, g, alpha, W, table=table)
+    bad = table._replace(slope=-table.slope)
+    _, _, _, da_bad, _ = O.backward_slab(q, k, v, g, alpha, W, table=bad)
     assert abs(da_bad - fd) > 1e-3 * abs(fd)
