@@ -77,9 +77,10 @@ def algo_bytes(D, in_bytes):
 class Stack:
     """Device buffers of every layer of one workload."""
 
-    def __init__(self, wl, window, layers, torch, F, I):
+    def __init__(self, wl, window, layers, torch, F, I, pattern="fib"):
         self.torch, self.F = torch, F
         self.wl, self.W, self.layers = wl, window, layers
+        self.pattern = F.PATTERNS[pattern]
         kind = {"linear": F.FSA_SCHEDULE_LINEAR, "coprime": F.FSA_SCHEDULE_COPRIME,
                 "fixed": F.FSA_SCHEDULE_FIXED}[wl.schedule]
         self.alphas = F.fsa_schedule(kind, wl.layers)
@@ -112,15 +113,16 @@ class Stack:
             p = {n: vp(x.data_ptr()) for n, x in t.items()}
             nws = t["ws"].numel()
             a = f32(float(self.alphas[l]))
-            fwd.append((lib.fsa_forward, (p["q"], p["k"], p["v"], dt, B, H, T, D, a,
-                                          self.W, p["out"], p["lse"], stream)))
-            dq.append((lib.fsa_backward_dq, (p["q"], p["k"], p["v"], p["dout"],
-                                             p["lse"], dt, B, H, T, D, a, self.W,
-                                             p["dq"], p["ws"], nws, stream)))
-            dkdv.append((lib.fsa_backward_dkdv, (p["q"], p["k"], p["v"], p["dout"],
-                                                 p["lse"], dt, B, H, T, D, a, self.W,
-                                                 p["dk"], p["dv"], p["dalpha"],
-                                                 p["ws"], nws, stream)))
+            pt = self.pattern
+            fwd.append((lib.fsa_forward_ex, (p["q"], p["k"], p["v"], dt, B, H, T, D, a,
+                                             self.W, pt, p["out"], p["lse"], stream)))
+            dq.append((lib.fsa_backward_dq_ex, (p["q"], p["k"], p["v"], p["dout"],
+                                                p["lse"], dt, B, H, T, D, a, self.W, pt,
+                                                p["dq"], p["ws"], nws, stream)))
+            dkdv.append((lib.fsa_backward_dkdv_ex, (p["q"], p["k"], p["v"], p["dout"],
+                                                    p["lse"], dt, B, H, T, D, a, self.W,
+                                                    pt, p["dk"], p["dv"], p["dalpha"],
+                                                    p["ws"], nws, stream)))
         # forward in layer order; backward in reverse layer order, dq stage then
         # dk/dv stage of each layer
         self.order = [("fwd",) + c for c in fwd]
@@ -258,14 +260,15 @@ def load_traffic(kernel, per_launch_tokens):
 def _oracle_layer(args):
     import numpy as np
     from oracle import fsa_oracle as O
-    q, k, v, g, alpha, W = args
+    q, k, v, g, alpha, W, base, mode = args
     B, H = q.shape[:2]
     t0 = time.perf_counter()
     for b in range(B):
         for h in range(H):
             sl = [x[b, h].astype(np.float64) for x in (q, k, v, g)]
-            O.forward_slab(sl[0], sl[1], sl[2], alpha, W)
-            O.backward_slab(sl[0], sl[1], sl[2], sl[3], alpha, W)
+            O.forward_slab(sl[0], sl[1], sl[2], alpha, W, base=base, mode=mode)
+            O.backward_slab(sl[0], sl[1], sl[2], sl[3], alpha, W, base=base,
+                            mode=mode)
     return time.perf_counter() - t0
 
 
@@ -273,7 +276,7 @@ def _noop(_):
     return os.getpid()
 
 
-def cpu_baseline(wl, window, alphas, layers):
+def cpu_baseline(wl, window, alphas, layers, pattern="fib"):
     """The fp64 oracle (forward + backward of every (b, h) slab) over whole
     layers of the workload, one layer per worker task."""
     from static_pattern_sparse_amd import inputs as I
@@ -283,7 +286,9 @@ def cpu_baseline(wl, window, alphas, layers):
     jobs = []
     for l in range(layers):
         x = I.workload_inputs(wl, l)
-        jobs.append((x["q"], x["k"], x["v"], x["dout"], float(alphas[l]), window))
+        base, _, mode = pattern.partition("-")
+        jobs.append((x["q"], x["k"], x["v"], x["dout"], float(alphas[l]), window,
+                     base, "round" if mode == "round" else "lerp"))
     ctx = multiprocessing.get_context("spawn")
     from concurrent.futures import ProcessPoolExecutor
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
@@ -309,6 +314,10 @@ def main():
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-t4096", action="store_true")
+    ap.add_argument("--pattern", default="fib",
+                    choices=["fib", "fib-round", "pow2", "pow2-round"],
+                    help="tap pattern: Fibonacci or power-of-two base, "
+                         "interpolated or rounded offsets (default fib)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (3 launches), whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the kernels' counters "
@@ -336,7 +345,7 @@ def main():
         torch.cuda.empty_cache()
 
     wl = I.WORKLOADS["linear16_bwd_bf16_b8h8t1024d64_w12"]
-    stack = Stack(wl, 12, args.layers, torch, F, I)
+    stack = Stack(wl, 12, args.layers, torch, F, I, args.pattern)
     print(f"[bench] {wl.name}: {args.layers} layers resident", file=sys.stderr, flush=True)
     ms_step, per_ms, counts = time_stack(stack, args.steps, args.warmup, torch)
     value, kernels, frac = summarise(stack, ms_step, per_ms)
@@ -345,7 +354,8 @@ def main():
     dom = max(per_ms, key=lambda n: per_ms[n])
     th = wl.B * wl.H * wl.T
     achieved = kernels[dom]["gbs"]
-    traffic = load_traffic(dom, th)
+    # the committed counter summaries were taken with the Fibonacci table
+    traffic = load_traffic(dom, th) if args.pattern == "fib" else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -360,7 +370,7 @@ def main():
         "data": "synthetic (seeded N(0,1) post-RoPE q, k; v; dout)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "D": wl.D,
                    "W": 12, "layers": args.layers, "schedule": wl.schedule,
-                   "pass": "forward+backward"},
+                   "pattern": args.pattern, "pass": "forward+backward"},
         "roofline": roofline,
         "hbm_frac": frac,
         "kernels": kernels,
@@ -371,7 +381,7 @@ def main():
 
     if not args.skip_t4096:
         wl2 = I.WORKLOADS["coprime16_bf16_b4h8t4096d64_w6-12"]
-        st2 = Stack(wl2, 12, args.layers, torch, F, I)
+        st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern)
         print(f"[bench] {wl2.name} W=12 resident", file=sys.stderr, flush=True)
         ms2, per2, _ = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
         v2, k2, f2 = summarise(st2, ms2, per2)
@@ -383,7 +393,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, 12, F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 16),
-                                           args.layers)
+                                           args.layers, args.pattern)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -66,7 +66,38 @@ extern "C" {
 #define FSA_DTYPE_F32 0
 #define FSA_DTYPE_BF16 1
 
-#define FSA_NUM_TAPS 15 /* Fibonacci distances 1, 2, 3, 5, ..., 987 */
+#define FSA_NUM_TAPS 15 /* base distances per pattern (both bases) */
+
+/*
+ * Tap patterns: a base list and a mode, or-ed together. The entry points
+ * without the _ex suffix use FSA_PATTERN_FIB.
+ *   FSA_BASE_FIBONACCI  f = 1, 2, 3, 5, ..., 987 [DSFS: Methodology >
+ *                       Architecture and attention > Attended set].
+ *   FSA_BASE_POW2       f = 1, 2, 4, ..., 16384, the power-of-two (log-sparse)
+ *                       control [DSFS: Methodology > Control variables]; the
+ *                       ladder runs past 987 because the page names 1024 and
+ *                       2048 as offsets that a 4096-token evaluation reaches
+ *                       [DSFS: Core contributions and results > 3. Length
+ *                       extrapolation, base sensitivity]; fifteen terms, as
+ *                       many as the Fibonacci list.
+ *   FSA_MODE_LERP       fractional distances interpolate rows a = i - ceil(d)
+ *                       and a + 1 [DSFS: Methodology > Architecture and
+ *                       attention > Implementation].
+ *   FSA_MODE_ROUND      integer offsets round(d) (nearest, ties to even), the
+ *                       mask form of the static runs [DSFS: Core contributions
+ *                       and results > 2. Learned dilation is inert,
+ *                       efficiency]; the attended rows do not move with alpha,
+ *                       so dalpha is 0.
+ * In every pattern a term with alpha*f < W is dropped, and for query i a tap
+ * applies when i >= c (c the distance of its lower row).
+ */
+#define FSA_BASE_FIBONACCI 0
+#define FSA_BASE_POW2 1
+#define FSA_BASE_MASK 1
+#define FSA_MODE_LERP 0
+#define FSA_MODE_ROUND 2
+#define FSA_MODE_MASK 2
+#define FSA_PATTERN_FIB (FSA_BASE_FIBONACCI | FSA_MODE_LERP)
 
 /*
  * fsa_schedule -- per-layer alpha table, host only.
@@ -96,6 +127,16 @@ int fsa_schedule(int kind, int num_layers, float alpha_min, float alpha_max,
  */
 int fsa_offsets(float alpha, int window, int32_t* c_out, float* t_out,
                 uint8_t* keep_out);
+
+/*
+ * fsa_offsets_ex -- fsa_offsets for any tap pattern (FSA_BASE_* | FSA_MODE_*):
+ * c_out[k] is the lower-row distance of base term k (round(alpha*f_k) in
+ * FSA_MODE_ROUND), t_out[k] the upper-row weight (0 in FSA_MODE_ROUND),
+ * keep_out[k] = (alpha*f_k >= W). Returns FSA_ERR_INVALID_ARG also for an
+ * unknown pattern.
+ */
+int fsa_offsets_ex(int pattern, float alpha, int window, int32_t* c_out,
+                   float* t_out, uint8_t* keep_out);
 
 /*
  * fsa_forward -- out, lse of one layer.
@@ -157,6 +198,32 @@ int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                       int H, int T, int D, float alpha, int window, float* dk,
                       float* dv, float* dalpha, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * _ex variants: the same calls with a tap pattern (FSA_BASE_* | FSA_MODE_*)
+ * after `window`; arguments, layouts and errors as above, plus
+ * FSA_ERR_INVALID_ARG for an unknown pattern. In FSA_MODE_ROUND dalpha is
+ * written as 0.
+ */
+int fsa_forward_ex(const void* q, const void* k, const void* v, int dtype,
+                   int B, int H, int T, int D, float alpha, int window,
+                   int pattern, float* out, float* lse, void* stream);
+int fsa_backward_ex(const void* q, const void* k, const void* v,
+                    const void* dout, const float* lse, int dtype, int B, int H,
+                    int T, int D, float alpha, int window, int pattern,
+                    float* dq, float* dk, float* dv, float* dalpha,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int fsa_backward_dq_ex(const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, int dtype, int B,
+                       int H, int T, int D, float alpha, int window,
+                       int pattern, float* dq, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int fsa_backward_dkdv_ex(const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, int dtype, int B,
+                         int H, int T, int D, float alpha, int window,
+                         int pattern, float* dk, float* dv, float* dalpha,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* fsa_status_string -- static text for a status code. */
 const char* fsa_status_string(int status);

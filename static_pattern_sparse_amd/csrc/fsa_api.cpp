@@ -19,6 +19,60 @@ namespace {
 constexpr int kFib[kNumTaps] = {1,  2,  3,   5,   8,   13,  21, 34,
                                 55, 89, 144, 233, 377, 610, 987};
 
+// Methodology > Control variables: the power-of-two (log-sparse) control base.
+// Fifteen terms 1, 2, 4, ..., 16384, as many as the Fibonacci list. The page's
+// examples of offsets that only a longer evaluation reaches (1024 and 2048 at
+// four times a 1024 training length, Results > Length extrapolation, base
+// sensitivity) need a ladder that goes on past 987; terms beyond a sequence's
+// length attend nothing.
+constexpr int kNumPow2 = 15;
+constexpr int kPow2[kNumPow2] = {1,   2,   4,    8,    16,   32,   64,  128,
+                                 256, 512, 1024, 2048, 4096, 8192, 16384};
+
+// Base distances of a pattern: the list and its length.
+const int* base_list(int pattern, int* n) {
+  if ((pattern & FSA_BASE_MASK) == FSA_BASE_POW2) {
+    *n = kNumPow2;
+    return kPow2;
+  }
+  *n = kNumTaps;
+  return kFib;
+}
+
+bool pattern_ok(int pattern) {
+  return (pattern & ~(FSA_BASE_MASK | FSA_MODE_MASK)) == 0 &&
+         (pattern & FSA_BASE_MASK) <= FSA_BASE_POW2;
+}
+
+// Nearest integer to d >= 0, ties to the even neighbour.
+double round_even(double d) {
+  const double f = std::floor(d);
+  const double r = d - f;
+  if (r > 0.5) return f + 1.0;
+  if (r < 0.5) return f;
+  return std::fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+// One base distance at scale alpha: the distance c of the lower row, the
+// weight t of the upper row and the slope d(position)/d(alpha). The distance
+// alpha*f is exact in fp64 (24 + 15 significant bits).
+//   interpolated (Methodology > Architecture and attention > Implementation):
+//     c = ceil(d), t = c - d, slope -f;
+//   rounded (the integer offsets that let static runs take a fused mask path,
+//   Core contributions and results > 2. Learned dilation is inert, efficiency):
+//     c = round(d), t = 0, slope 0 -- the attended rows do not move with alpha.
+void tap_of(int pattern, double d, double f, double* c, double* t, double* slope) {
+  if (pattern & FSA_MODE_ROUND) {
+    *c = round_even(d);
+    *t = 0.0;
+    *slope = 0.0;
+  } else {
+    *c = std::ceil(d);
+    *t = *c - d;
+    *slope = -f;
+  }
+}
+
 thread_local int g_last_hip_error = 0;
 
 bool alpha_ok(float a) { return std::isfinite(a) && a >= 0.5f && a <= 1.5f; }
@@ -32,21 +86,22 @@ int gcd(int a, int b) {
   return a < 0 ? -a : a;
 }
 
-// Tap table of one layer. The distance alpha*f is formed in fp64 from the fp32
-// alpha; 24 + 10 significant bits fit in fp64, so it is exact, and so are
-// ceil(d) - d and 1 - (ceil(d) - d). Each weight is then rounded once to fp32.
-void build_taps(float alpha, int window, Taps* t) {
+// Tap table of one layer: the kept base distances (alpha*f >= W), ascending.
+// Each weight is rounded once to fp32 from its exact fp64 value.
+void build_taps(int pattern, float alpha, int window, Taps* t) {
+  int nb = 0;
+  const int* f = base_list(pattern, &nb);
   t->n = 0;
-  for (int k = 0; k < kNumTaps; ++k) {
-    const double d = static_cast<double>(alpha) * kFib[k];
+  for (int k = 0; k < nb; ++k) {
+    const double d = static_cast<double>(alpha) * f[k];
     if (d < static_cast<double>(window)) continue;   // inside the window
-    const double c = std::ceil(d);
-    const double hi = c - d;
+    double c, hi, slope;
+    tap_of(pattern, d, f[k], &c, &hi, &slope);
     const int n = t->n++;
     t->c[n] = static_cast<int>(c);
     t->w_hi[n] = static_cast<float>(hi);
     t->w_lo[n] = static_cast<float>(1.0 - hi);
-    t->neg_f[n] = -static_cast<float>(kFib[k]);
+    t->neg_f[n] = static_cast<float>(slope);
   }
 }
 
@@ -91,8 +146,9 @@ BwdWorkspace bwd_layout(int B, int H, int T, int D, int dtype);
 // Checks shared by the backward stages; fills *a on success.
 int check_bwd(const void* q, const void* k, const void* v, const void* dout,
               const float* lse, int dtype, int B, int H, int T, int D,
-              float alpha, int window, void* workspace, size_t workspace_bytes,
-              BwdArgs* a) {
+              float alpha, int window, int pattern, void* workspace,
+              size_t workspace_bytes, BwdArgs* a) {
+  if (!pattern_ok(pattern)) return FSA_ERR_INVALID_ARG;
   int st = check_shape(dtype, B, H, T, D, alpha, window);
   if (st != FSA_OK) return st;
   a->empty = static_cast<long long>(B) * H * T == 0;
@@ -105,7 +161,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* dout,
   if (workspace == nullptr || workspace_bytes < ws.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FSA_ERR_WORKSPACE;
-  build_taps(alpha, window, &a->taps);
+  build_taps(pattern, alpha, window, &a->taps);
   a->pr = make_problem(B, H, T, D, window);
   char* wsb = static_cast<char*>(workspace);
   a->delta = reinterpret_cast<float*>(wsb + ws.delta_off);
@@ -210,23 +266,33 @@ int fsa_schedule(int kind, int num_layers, float alpha_min, float alpha_max,
   return FSA_OK;
 }
 
-int fsa_offsets(float alpha, int window, int32_t* c_out, float* t_out,
-                uint8_t* keep_out) {
-  if (!c_out || !t_out || !keep_out || window < 1 || !alpha_ok(alpha))
+int fsa_offsets_ex(int pattern, float alpha, int window, int32_t* c_out,
+                   float* t_out, uint8_t* keep_out) {
+  if (!c_out || !t_out || !keep_out || window < 1 || !alpha_ok(alpha) ||
+      !pattern_ok(pattern))
     return FSA_ERR_INVALID_ARG;
-  for (int k = 0; k < kNumTaps; ++k) {
-    const double d = static_cast<double>(alpha) * kFib[k];
-    const double c = std::ceil(d);
+  int nb = 0;
+  const int* f = base_list(pattern, &nb);
+  for (int k = 0; k < nb; ++k) {
+    const double d = static_cast<double>(alpha) * f[k];
+    double c, t, slope;
+    tap_of(pattern, d, f[k], &c, &t, &slope);
     c_out[k] = static_cast<int32_t>(c);
-    t_out[k] = static_cast<float>(c - d);
+    t_out[k] = static_cast<float>(t);
     keep_out[k] = d >= static_cast<double>(window) ? 1 : 0;
   }
   return FSA_OK;
 }
 
-int fsa_forward(const void* q, const void* k, const void* v, int dtype, int B,
-                int H, int T, int D, float alpha, int window, float* out,
-                float* lse, void* stream) {
+int fsa_offsets(float alpha, int window, int32_t* c_out, float* t_out,
+                uint8_t* keep_out) {
+  return fsa_offsets_ex(FSA_PATTERN_FIB, alpha, window, c_out, t_out, keep_out);
+}
+
+int fsa_forward_ex(const void* q, const void* k, const void* v, int dtype,
+                   int B, int H, int T, int D, float alpha, int window,
+                   int pattern, float* out, float* lse, void* stream) {
+  if (!pattern_ok(pattern)) return FSA_ERR_INVALID_ARG;
   int st = check_shape(dtype, B, H, T, D, alpha, window);
   if (st != FSA_OK) return st;
   if (static_cast<long long>(B) * H * T == 0) return FSA_OK;
@@ -235,10 +301,17 @@ int fsa_forward(const void* q, const void* k, const void* v, int dtype, int B,
       !aligned16(lse))
     return FSA_ERR_INVALID_ARG;
   Taps taps;
-  build_taps(alpha, window, &taps);
+  build_taps(pattern, alpha, window, &taps);
   const Problem pr = make_problem(B, H, T, D, window);
   return hip_status(launch_forward(q, k, v, dtype, pr, taps, out, lse,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int fsa_forward(const void* q, const void* k, const void* v, int dtype, int B,
+                int H, int T, int D, float alpha, int window, float* out,
+                float* lse, void* stream) {
+  return fsa_forward_ex(q, k, v, dtype, B, H, T, D, alpha, window,
+                        FSA_PATTERN_FIB, out, lse, stream);
 }
 
 size_t fsa_backward_workspace_size(int B, int H, int T, int D, int dtype) {
@@ -247,13 +320,14 @@ size_t fsa_backward_workspace_size(int B, int H, int T, int D, int dtype) {
   return bwd_workspace_layout(B, H, T, D, dtype).total;
 }
 
-int fsa_backward_dq(const void* q, const void* k, const void* v,
-                    const void* dout, const float* lse, int dtype, int B, int H,
-                    int T, int D, float alpha, int window, float* dq,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int fsa_backward_dq_ex(const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, int dtype, int B,
+                       int H, int T, int D, float alpha, int window,
+                       int pattern, float* dq, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   BwdArgs a;
   int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
-                     workspace, workspace_bytes, &a);
+                     pattern, workspace, workspace_bytes, &a);
   if (st != FSA_OK || a.empty) return st;
   if (!dq || !aligned16(dq)) return FSA_ERR_INVALID_ARG;
   return hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
@@ -261,14 +335,15 @@ int fsa_backward_dq(const void* q, const void* k, const void* v,
                                   static_cast<hipStream_t>(stream)));
 }
 
-int fsa_backward_dkdv(const void* q, const void* k, const void* v,
-                      const void* dout, const float* lse, int dtype, int B,
-                      int H, int T, int D, float alpha, int window, float* dk,
-                      float* dv, float* dalpha, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int fsa_backward_dkdv_ex(const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, int dtype, int B,
+                         int H, int T, int D, float alpha, int window,
+                         int pattern, float* dk, float* dv, float* dalpha,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream) {
   BwdArgs a;
   int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
-                     workspace, workspace_bytes, &a);
+                     pattern, workspace, workspace_bytes, &a);
   if (st != FSA_OK) return st;
   if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -278,14 +353,14 @@ int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                                     dtype, a.pr, a.taps, dk, dv, dalpha, s));
 }
 
-int fsa_backward(const void* q, const void* k, const void* v,
-                 const void* dout, const float* lse, int dtype, int B, int H,
-                 int T, int D, float alpha, int window, float* dq, float* dk,
-                 float* dv, float* dalpha, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+int fsa_backward_ex(const void* q, const void* k, const void* v,
+                    const void* dout, const float* lse, int dtype, int B, int H,
+                    int T, int D, float alpha, int window, int pattern,
+                    float* dq, float* dk, float* dv, float* dalpha,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   BwdArgs a;
   int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
-                     workspace, workspace_bytes, &a);
+                     pattern, workspace, workspace_bytes, &a);
   if (st != FSA_OK) return st;
   if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
   if (!a.empty && (!dq || !dk || !dv || !aligned16(dq) || !aligned16(dk) ||
@@ -298,6 +373,35 @@ int fsa_backward(const void* q, const void* k, const void* v,
   if (st != FSA_OK) return st;
   return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, a.partials,
                                     dtype, a.pr, a.taps, dk, dv, dalpha, s));
+}
+
+int fsa_backward_dq(const void* q, const void* k, const void* v,
+                    const void* dout, const float* lse, int dtype, int B, int H,
+                    int T, int D, float alpha, int window, float* dq,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return fsa_backward_dq_ex(q, k, v, dout, lse, dtype, B, H, T, D, alpha,
+                            window, FSA_PATTERN_FIB, dq, workspace,
+                            workspace_bytes, stream);
+}
+
+int fsa_backward_dkdv(const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, int dtype, int B,
+                      int H, int T, int D, float alpha, int window, float* dk,
+                      float* dv, float* dalpha, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return fsa_backward_dkdv_ex(q, k, v, dout, lse, dtype, B, H, T, D, alpha,
+                              window, FSA_PATTERN_FIB, dk, dv, dalpha,
+                              workspace, workspace_bytes, stream);
+}
+
+int fsa_backward(const void* q, const void* k, const void* v,
+                 const void* dout, const float* lse, int dtype, int B, int H,
+                 int T, int D, float alpha, int window, float* dq, float* dk,
+                 float* dv, float* dalpha, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return fsa_backward_ex(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
+                         FSA_PATTERN_FIB, dq, dk, dv, dalpha, workspace,
+                         workspace_bytes, stream);
 }
 
 const char* fsa_status_string(int status) {

@@ -28,10 +28,23 @@ FSA_DTYPE_BF16 = 1
 
 NUM_TAPS = 15
 
+# tap patterns (base | mode), as in include/fsa.h
+FSA_BASE_FIBONACCI = 0
+FSA_BASE_POW2 = 1
+FSA_MODE_LERP = 0
+FSA_MODE_ROUND = 2
+FSA_PATTERN_FIB = FSA_BASE_FIBONACCI | FSA_MODE_LERP
+PATTERNS = {"fib": FSA_PATTERN_FIB,
+            "fib-round": FSA_BASE_FIBONACCI | FSA_MODE_ROUND,
+            "pow2": FSA_BASE_POW2 | FSA_MODE_LERP,
+            "pow2-round": FSA_BASE_POW2 | FSA_MODE_ROUND}
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsa.so")
-EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_forward",
-           "fsa_backward_workspace_size", "fsa_backward", "fsa_backward_dq",
-           "fsa_backward_dkdv", "fsa_status_string", "fsa_last_hip_error")
+EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_offsets_ex", "fsa_forward",
+           "fsa_forward_ex", "fsa_backward_workspace_size", "fsa_backward",
+           "fsa_backward_ex", "fsa_backward_dq", "fsa_backward_dq_ex",
+           "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_status_string",
+           "fsa_last_hip_error")
 
 _lib = None
 
@@ -60,6 +73,8 @@ def lib():
     L.fsa_offsets.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_int32),
                               ctypes.POINTER(f32), ctypes.POINTER(ctypes.c_uint8)]
     L.fsa_offsets.restype = i32
+    L.fsa_offsets_ex.argtypes = [i32] + L.fsa_offsets.argtypes
+    L.fsa_offsets_ex.restype = i32
     L.fsa_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                               vp, vp, vp]
     L.fsa_forward.restype = i32
@@ -74,6 +89,14 @@ def lib():
     L.fsa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     f32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.fsa_backward_dkdv.restype = i32
+    # _ex variants: the tap pattern follows `window` (argument 10 or 12)
+    L.fsa_forward_ex.argtypes = L.fsa_forward.argtypes[:10] + [i32] + L.fsa_forward.argtypes[10:]
+    L.fsa_forward_ex.restype = i32
+    for name in ("fsa_backward", "fsa_backward_dq", "fsa_backward_dkdv"):
+        base = getattr(L, name).argtypes
+        ex = getattr(L, name + "_ex")
+        ex.argtypes = base[:12] + [i32] + base[12:]
+        ex.restype = i32
     L.fsa_status_string.argtypes = [i32]
     L.fsa_status_string.restype = ctypes.c_char_p
     L.fsa_last_hip_error.argtypes = []
@@ -96,11 +119,11 @@ def fsa_schedule(kind, num_layers=16, alpha_min=0.5, alpha_max=1.5, stride=7):
     return out
 
 
-def fsa_offsets(alpha, window):
+def fsa_offsets(alpha, window, pattern=FSA_PATTERN_FIB):
     c = np.zeros(NUM_TAPS, dtype=np.int32)
     t = np.zeros(NUM_TAPS, dtype=np.float32)
     keep = np.zeros(NUM_TAPS, dtype=np.uint8)
-    st = lib().fsa_offsets(float(alpha), int(window),
+    st = lib().fsa_offsets_ex(int(pattern), float(alpha), int(window),
                            c.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                            t.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                            keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
@@ -136,7 +159,8 @@ def _shape(q):
     return tuple(int(s) for s in q.shape)
 
 
-def fsa_forward(q, k, v, alpha, window, out=None, lse=None, stream=None):
+def fsa_forward(q, k, v, alpha, window, out=None, lse=None, stream=None,
+                pattern=FSA_PATTERN_FIB):
     """out [B,H,T,D] fp32 and lse [B,H,T] fp32 of one layer."""
     import torch
     B, H, T, D = _shape(q)
@@ -147,9 +171,9 @@ def fsa_forward(q, k, v, alpha, window, out=None, lse=None, stream=None):
         out = torch.empty((B, H, T, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    st = lib().fsa_forward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T,
-                           D, float(alpha), int(window), _ptr(out), _ptr(lse),
-                           _stream(stream))
+    st = lib().fsa_forward_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H,
+                              T, D, float(alpha), int(window), int(pattern),
+                              _ptr(out), _ptr(lse), _stream(stream))
     _check("fsa_forward", st)
     return out, lse
 
@@ -160,7 +184,8 @@ def fsa_backward_workspace_size(B, H, T, D, dtype_code):
 
 
 def fsa_backward(q, k, v, dout, lse, alpha, window, dq=None, dk=None, dv=None,
-                 dalpha=None, workspace=None, stream=None):
+                 dalpha=None, workspace=None, stream=None,
+                 pattern=FSA_PATTERN_FIB):
     """dq, dk, dv [B,H,T,D] fp32 and dalpha [1] fp32 of one layer."""
     import torch
     B, H, T, D = _shape(q)
@@ -177,8 +202,9 @@ def fsa_backward(q, k, v, dout, lse, alpha, window, dq=None, dk=None, dv=None,
     nbytes = fsa_backward_workspace_size(B, H, T, D, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib().fsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), dt,
-                            B, H, T, D, float(alpha), int(window), _ptr(dq),
+    st = lib().fsa_backward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                            dt, B, H, T, D, float(alpha), int(window),
+                            int(pattern), _ptr(dq),
                             _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(workspace),
                             workspace.numel() * workspace.element_size(),
                             _stream(stream))
@@ -191,25 +217,27 @@ def _ws_bytes(ws):
 
 
 def fsa_backward_dq(q, k, v, dout, lse, alpha, window, dq, workspace,
-                    stream=None):
+                    stream=None, pattern=FSA_PATTERN_FIB):
     """Stage 1 of the backward pass: dq, plus per-row terms and dalpha
     partials in `workspace`."""
     B, H, T, D = _shape(q)
-    st = lib().fsa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
-                               _dtype_code(q), B, H, T, D, float(alpha),
-                               int(window), _ptr(dq), _ptr(workspace),
+    st = lib().fsa_backward_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                               _ptr(lse), _dtype_code(q), B, H, T, D,
+                               float(alpha), int(window), int(pattern),
+                               _ptr(dq), _ptr(workspace),
                                _ws_bytes(workspace), _stream(stream))
     _check("fsa_backward_dq", st)
 
 
 def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, dalpha,
-                      workspace, stream=None):
+                      workspace, stream=None, pattern=FSA_PATTERN_FIB):
     """Stage 2 of the backward pass: dk, dv, and dalpha[0] from the stage-1
     partials."""
     B, H, T, D = _shape(q)
-    st = lib().fsa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+    st = lib().fsa_backward_dkdv_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                  _ptr(lse), _dtype_code(q), B, H, T, D,
-                                 float(alpha), int(window), _ptr(dk), _ptr(dv),
+                                 float(alpha), int(window), int(pattern),
+                                 _ptr(dk), _ptr(dv),
                                  _ptr(dalpha), _ptr(workspace),
                                  _ws_bytes(workspace), _stream(stream))
     _check("fsa_backward_dkdv", st)

@@ -55,7 +55,7 @@ def test_schedule_bit_exact_vs_oracle(kind, L):
 @pytest.mark.parametrize("W", [1, 6, 12, 100])
 def test_offsets_vs_oracle(alpha, W):
     c, t, keep = F.fsa_offsets(alpha, W)
-    d_r, c_r, t_r, keep_r = O.offset_table(alpha, W)
+    d_r, c_r, t_r, keep_r, _ = O.offset_table(alpha, W)
     assert np.array_equal(c, c_r)
     assert np.array_equal(keep, keep_r)
     assert np.array_equal(t, t_r.astype(np.float32))
@@ -140,3 +140,42 @@ def test_workspace_size():
     assert F.fsa_backward_workspace_size(1, 1, 16, 96, 1) == 0
     big = F.fsa_backward_workspace_size(1, 16, 65536, 128, 1)
     assert big >= 16 * 65536 * 4
+
+
+# ---------------------------------------------------------------- tap patterns
+_ORACLE_PATTERN = {"fib": ("fib", "lerp"), "fib-round": ("fib", "round"),
+                   "pow2": ("pow2", "lerp"), "pow2-round": ("pow2", "round")}
+
+
+@pytest.mark.parametrize("name", sorted(_ORACLE_PATTERN))
+@pytest.mark.parametrize("alpha", [0.5, 1.0, 1.5, 0.7317, 0.5666667, 1.2913])
+@pytest.mark.parametrize("W", [1, 6, 12])
+def test_offsets_ex_vs_oracle(name, alpha, W):
+    c, t, keep = F.fsa_offsets(alpha, W, F.PATTERNS[name])
+    base, mode = _ORACLE_PATTERN[name]
+    tab = O.offset_table(alpha, W, base=base, mode=mode)
+    assert np.array_equal(c, tab.c)
+    assert np.array_equal(keep, tab.keep)
+    assert np.array_equal(t, tab.t.astype(np.float32))
+
+
+def test_pattern_validation_codes():
+    with pytest.raises(F.FsaError):
+        F.fsa_offsets(1.0, 8, 4)
+    with pytest.raises(F.FsaError):
+        F.fsa_offsets(1.0, 8, -1)
+    lib = F.lib()
+    args = [ctypes.c_void_p(FAKE)] * 3 + [1, 1, 1, 16, 64, 1.0, 4]
+    for bad in (4, 8, -1):
+        assert lib.fsa_forward_ex(*args, bad, ctypes.c_void_p(FAKE),
+                                  ctypes.c_void_p(FAKE), None) == F.FSA_ERR_INVALID_ARG
+    bwd = [ctypes.c_void_p(FAKE)] * 5 + [1, 1, 1, 16, 64, 1.0, 4]
+    out4 = [ctypes.c_void_p(FAKE)] * 5 + [1 << 20, None]
+    assert lib.fsa_backward_ex(*bwd, 4, *out4) == F.FSA_ERR_INVALID_ARG
+    assert lib.fsa_backward_dq_ex(*bwd, 4, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                  1 << 20, None) == F.FSA_ERR_INVALID_ARG
+    assert lib.fsa_backward_dkdv_ex(*bwd, 4, *out4[1:]) == F.FSA_ERR_INVALID_ARG
+    # every valid pattern passes validation up to the first bad argument
+    for p in F.PATTERNS.values():
+        assert lib.fsa_forward_ex(*args[:-1], 0, p, ctypes.c_void_p(FAKE),
+                                  ctypes.c_void_p(FAKE), None) == F.FSA_ERR_INVALID_ARG

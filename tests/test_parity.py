@@ -42,19 +42,25 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def gpu_forward(x, dtype, alpha, W):
+# pattern name -> (oracle base, oracle mode); the library's codes are
+# static_pattern_sparse_amd.fsa.PATTERNS
+ORACLE_PATTERN = {"fib": ("fib", "lerp"), "fib-round": ("fib", "round"),
+                  "pow2": ("pow2", "lerp"), "pow2-round": ("pow2", "round")}
+
+
+def gpu_forward(x, dtype, alpha, W, pattern="fib"):
     torch = _torch()
     from static_pattern_sparse_amd import fsa as F
     q, k, v = (I.to_device(x[n], dtype) for n in ("q", "k", "v"))
     B, H, T, D = q.shape
     out = torch.full((B, H, T, D), float("nan"), device="cuda")
     lse = torch.full((B, H, T), float("nan"), device="cuda")
-    F.fsa_forward(q, k, v, alpha, W, out=out, lse=lse)
+    F.fsa_forward(q, k, v, alpha, W, out=out, lse=lse, pattern=F.PATTERNS[pattern])
     torch.cuda.synchronize()
     return out, lse
 
 
-def gpu_backward(x, dtype, alpha, W, lse):
+def gpu_backward(x, dtype, alpha, W, lse, pattern="fib"):
     torch = _torch()
     from static_pattern_sparse_amd import fsa as F
     q, k, v, g = (I.to_device(x[n], dtype) for n in ("q", "k", "v", "dout"))
@@ -62,7 +68,8 @@ def gpu_backward(x, dtype, alpha, W, lse):
     nan = lambda: torch.full((B, H, T, D), float("nan"), device="cuda")
     dq, dk, dv = nan(), nan(), nan()
     da = torch.full((1,), float("nan"), device="cuda")
-    F.fsa_backward(q, k, v, g, lse, alpha, W, dq=dq, dk=dk, dv=dv, dalpha=da)
+    F.fsa_backward(q, k, v, g, lse, alpha, W, dq=dq, dk=dk, dv=dv, dalpha=da,
+                   pattern=F.PATTERNS[pattern])
     torch.cuda.synchronize()
     return dq, dk, dv, da
 
@@ -80,20 +87,23 @@ def _maxerr(a, b):
     return float(np.abs(a - b).max()) if a.size else 0.0
 
 
-def check_forward(x, dtype, alpha, W):
-    out, lse = gpu_forward(x, dtype, alpha, W)
+def check_forward(x, dtype, alpha, W, pattern="fib"):
+    out, lse = gpu_forward(x, dtype, alpha, W, pattern)
     xd = _f64(x)
-    ro, rl = O.forward(xd["q"], xd["k"], xd["v"], alpha, W)
+    base, mode = ORACLE_PATTERN[pattern]
+    ro, rl = O.forward(xd["q"], xd["k"], xd["v"], alpha, W, base=base, mode=mode)
     eo, el = _maxerr(_np(out), ro), _maxerr(_np(lse), rl)
     assert eo <= TOL[dtype], f"out err {eo}"
     assert el <= TOL[dtype], f"lse err {el}"
     return out, lse
 
 
-def check_backward(x, dtype, alpha, W, lse):
-    dq, dk, dv, da = gpu_backward(x, dtype, alpha, W, lse)
+def check_backward(x, dtype, alpha, W, lse, pattern="fib"):
+    dq, dk, dv, da = gpu_backward(x, dtype, alpha, W, lse, pattern)
     xd = _f64(x)
-    rq, rk, rv, ra = O.backward(xd["q"], xd["k"], xd["v"], xd["dout"], alpha, W)
+    base, mode = ORACLE_PATTERN[pattern]
+    rq, rk, rv, ra = O.backward(xd["q"], xd["k"], xd["v"], xd["dout"], alpha, W,
+                                base=base, mode=mode)
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         e = _maxerr(_np(g), r)
         assert e <= TOL[dtype], f"{name} err {e}"
@@ -133,6 +143,34 @@ def test_forward_backward_small(B, H, T, D, dtype, alpha, W):
     x = _rand_inputs(B, H, T, D, dtype, T % 7)
     out, lse = check_forward(x, dtype, alpha, W)
     check_backward(x, dtype, alpha, W, lse)
+
+
+# the power-of-two control base and the rounded (mask) mode: same kernels,
+# another tap table
+PATTERN_CASES = [
+    # B, H, T, D, dtype, alpha, W, pattern
+    (1, 2, 600, 64, "bf16", 0.7317, 12, "pow2"),
+    (1, 2, 1100, 64, "bf16", 1.0, 8, "pow2"),
+    (1, 1, 2100, 64, "bf16", 0.5666667, 12, "pow2"),     # reaches 1024 and 2048
+    (1, 2, 500, 64, "bf16", 0.5, 6, "fib-round"),        # ties to even
+    (1, 2, 777, 128, "bf16", 1.2913, 10, "fib-round"),
+    (1, 1, 1300, 64, "bf16", 0.8333333, 12, "pow2-round"),
+    (2, 1, 31, 64, "bf16", 1.5, 3, "pow2-round"),
+    (1, 1, 300, 64, "f32", 0.7317, 5, "pow2"),
+    (1, 1, 300, 128, "f32", 0.7317, 5, "fib-round"),
+    (1, 1, 400, 64, "bf16", 0.7317, 40, "pow2-round"),  # window past the tile kernels
+]
+
+
+@pytest.mark.parametrize("B,H,T,D,dtype,alpha,W,pattern", PATTERN_CASES)
+def test_patterns_forward_backward(B, H, T, D, dtype, alpha, W, pattern):
+    _say("pattern", pattern, B, H, T, D, dtype, alpha, W)
+    alpha = float(np.float32(alpha))
+    x = _rand_inputs(B, H, T, D, dtype, T % 5)
+    out, lse = check_forward(x, dtype, alpha, W, pattern)
+    _, _, _, da = check_backward(x, dtype, alpha, W, lse, pattern)
+    if pattern.endswith("round"):
+        assert float(da.item()) == 0.0
 
 
 def test_forward_deterministic_bitwise():
@@ -228,7 +266,7 @@ def test_workload_coprime16_t4096(layer, W):
 
 
 def _sample_rows(T, alpha, W, seed):
-    d, c, t, keep = O.offset_table(alpha, W)
+    d, c, t, keep, _ = O.offset_table(alpha, W)
     rows = {0, 1, 2, W - 1, W, W + 1, T - 2, T - 1}
     for ck in c[keep]:
         rows |= {int(ck) - 1, int(ck), int(ck) + 1, T - int(ck) - 1, T - int(ck)}
