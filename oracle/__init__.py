@@ -5,6 +5,6 @@ may import this package. It shares no code with the HIP library.
 """
 from .fsa_oracle import (BASES, FIB, MODES, POW2, SCHEDULE_COPRIME,  # noqa: F401
                          SCHEDULE_FIXED, TapTable,
-                         SCHEDULE_LINEAR, backward, backward_slab, dkdv_rows,
+                         SCHEDULE_LINEAR, backward, backward_slab, decode, dkdv_rows,
                          dq_rows, forward, forward_rows, forward_slab,
                          offset_table, schedule)

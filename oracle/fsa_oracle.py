@@ -449,3 +449,54 @@ def dkdv_rows(q, k, v, dout, alpha, window, rows, base="fib", mode="lerp"):
         dks.append(gk)
         dvs.append(gv)
     return np.array(dks), np.array(dvs)
+
+
+# ---------------------------------------------------------------------------
+# decode: one new query per (b, h) against cached rows
+# ---------------------------------------------------------------------------
+def decode(q, k_cache, v_cache, pos, alpha, window, base="fib", mode="lerp"):
+    """One decoding step: out[b, h] and lse[b, h] of the query q[b, h] at
+    position i = pos[b], which attends the cached key and value rows 0..i of
+    its (b, h) slab under the same rules as every other position: the window
+    rows i-W+1..i (from row 0 on) and the kept taps with i >= c_k, each tap
+    interpolating rows i-c_k and i-c_k+1 [DSFS: Methodology > Architecture and
+    attention > Attended set, Scaling, Implementation]. This is the step whose
+    latency the page compares between learned and static spacing [DSFS: Core
+    contributions and results > 2. Learned dilation is inert, efficiency].
+
+    q: [B, H, D]; k_cache, v_cache: [B, H, T_cap, D]; pos: B integers in
+    [0, T_cap). Rows past pos[b] are never read.
+    """
+    B, H, D = q.shape
+    table = offset_table(alpha, window, base=base, mode=mode)
+    scale = 1.0 / math.sqrt(D)
+    out = np.empty((B, H, D), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    for b in range(B):
+        i = int(pos[b])
+        if not 0 <= i < k_cache.shape[2]:
+            raise ValueError("position outside the cache")
+        for h in range(H):
+            qi, K, V = q[b, h], k_cache[b, h], v_cache[b, h]
+            scores, values = [], []
+            for w in range(window):              # window rows, newest first
+                j = i - w
+                if j < 0:
+                    break
+                scores.append(scale * float(qi @ K[j]))
+                values.append(V[j])
+            for n in range(len(table.c)):        # kept taps that reach a row
+                c = int(table.c[n])
+                if not table.keep[n] or i < c:
+                    continue
+                a, t = i - c, float(table.t[n])
+                key = (1.0 - t) * K[a] + t * K[a + 1]
+                val = (1.0 - t) * V[a] + t * V[a + 1]
+                scores.append(scale * float(qi @ key))
+                values.append(val)
+            s = np.array(scores)
+            mx = s.max()
+            lse[b, h] = mx + math.log(float(np.exp(s - mx).sum()))
+            p = np.exp(s - lse[b, h])
+            out[b, h] = (p[:, None] * np.array(values)).sum(axis=0)
+    return out, lse
