@@ -27,7 +27,11 @@ counted). The JSON line also carries:
                 peak; traffic from committed rocprofv3 counter summaries when
                 they match the current kernel source, else null;
   cpu_baseline  the fp64 oracle on the host cores over the same step;
-  t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12.
+  t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12;
+  decode        a decoding step (one new query per (b, h) in each of the 16
+                layers, B=8, H=8, caches of 4096 rows, W=12): time per step,
+                tokens per second and the mean launch time. Four distinct layer
+                caches serve the 16 layers in turn.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -138,6 +142,62 @@ class Stack:
                 raise RuntimeError(f"{name} returned status {st}")
         if ev is not None:
             ev.record(None)
+
+
+class DecodeStack:
+    """Device buffers of the decoding workload: one query per (b, h) and
+    layer against the caches; DECODE_CACHES distinct layer caches serve the
+    layers of one step in turn."""
+
+    def __init__(self, wl, window, torch, F, I, pattern="fib"):
+        import ctypes
+        self.wl, self.W, self.layers = wl, window, wl.layers
+        self.alphas = F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, wl.layers)
+        self.pattern = F.PATTERNS[pattern]
+        B, H, T, D = wl.B, wl.H, wl.T, wl.D
+        self.caches = []
+        for c in range(I.DECODE_CACHES):
+            x = I.decode_inputs(wl, c)
+            t = {n: I.to_device(x[n], wl.dtype) for n in ("q", "k", "v")}
+            t["pos"] = torch.from_numpy(x["pos"]).to("cuda")
+            self.caches.append(t)
+        self.positions = x["pos"]
+        f32t = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+        self.outs = [(f32t(B, H, D), f32t(B, H)) for _ in range(wl.layers)]
+        lib = F.lib()
+        vp, f32 = ctypes.c_void_p, ctypes.c_float
+        dt = F.FSA_DTYPE_BF16 if wl.dtype == "bf16" else F.FSA_DTYPE_F32
+        stream = vp(torch.cuda.current_stream().cuda_stream)
+        self.order = []
+        for l in range(wl.layers):
+            t = self.caches[l % len(self.caches)]
+            o, ls = self.outs[l]
+            p = {n: vp(x.data_ptr()) for n, x in t.items()}
+            self.order.append(("decode", lib.fsa_decode,
+                               (p["q"], p["k"], p["v"], dt, B, H, T, D, p["pos"],
+                                f32(float(self.alphas[l])), window, self.pattern,
+                                vp(o.data_ptr()), vp(ls.data_ptr()), stream)))
+        # rows each (b, h) query reads: its window rows and one or two rows per
+        # reaching tap (two when the distance is fractional)
+        self.rows_per_step = 0
+        for l in range(wl.layers):
+            c, tt, keep = F.fsa_offsets(float(self.alphas[l]), window, self.pattern)
+            for i in self.positions:
+                i = int(i)
+                self.rows_per_step += H * (min(window, i + 1) + sum(
+                    (2 if tt[n] != 0 else 1) for n in range(len(c))
+                    if keep[n] and c[n] <= i))
+
+    step = Stack.step
+
+    def bytes_per_step(self):
+        """Algorithmic bytes of one step: every row read once (K and V), the
+        queries, out and lse."""
+        wl = self.wl
+        in_b = 2 if wl.dtype == "bf16" else 4
+        per_query = wl.D * in_b + 4 * wl.D + 4
+        return (self.rows_per_step * 2 * wl.D * in_b
+                + wl.layers * wl.B * wl.H * per_query)
 
 
 class Events:
@@ -314,6 +374,7 @@ def main():
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-t4096", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--pattern", default="fib",
                     choices=["fib", "fib-round", "pow2", "pow2-round"],
                     help="tap pattern: Fibonacci or power-of-two base, "
@@ -388,6 +449,25 @@ def main():
         res["t4096"] = {"workload": wl2.name + " (W=12)", "value": round(v2, 1),
                         "ms_per_step": round(ms2, 4), "hbm_frac": f2, "kernels": k2}
         del st2
+        torch.cuda.empty_cache()
+
+    if not args.skip_decode:
+        wl3 = I.WORKLOADS["decode16_bf16_b8h8t4096d64_w12"]
+        st3 = DecodeStack(wl3, 12, torch, F, I, args.pattern)
+        print(f"[bench] {wl3.name} resident", file=sys.stderr, flush=True)
+        ms3, per3, _ = time_stack(st3, max(20, args.steps * 5), max(5, args.warmup), torch)
+        launch_us = per3["decode"] * 1e3
+        nbytes = st3.bytes_per_step() / wl3.layers
+        res["decode"] = {
+            "workload": wl3.name, "layers": wl3.layers,
+            "positions": [int(p) for p in st3.positions],
+            "us_per_step": round(ms3 * 1e3, 2),
+            "tokens_per_s": round(wl3.B / (ms3 * 1e-3), 1),
+            "mean_launch_us": round(launch_us, 3),
+            "algorithmic_bytes_per_launch": int(nbytes),
+            "gbs": round(nbytes / (launch_us * 1e-6) / 1e9, 1),
+            "bound": "latency"}
+        del st3
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

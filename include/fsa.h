@@ -225,6 +225,31 @@ int fsa_backward_dkdv_ex(const void* q, const void* k, const void* v,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * fsa_decode -- one decoding step: a new query per (b, h) against the cached
+ * rows of its slab.
+ * [DSFS: Methodology > Architecture and attention > Attended set, Scaling,
+ * Implementation; Core contributions and results > 2. Learned dilation is
+ * inert, efficiency (the inference latency of this step)]
+ *   q         device [B][H][D] of `dtype`: the post-RoPE query of position
+ *             pos[b], 16-byte aligned.
+ *   k_cache, v_cache  device [B][H][T_cap][D] of `dtype`, 16-byte aligned:
+ *             rows 0..pos[b] of slab (b, h) hold the keys (post-RoPE) and
+ *             values of positions 0..pos[b]; rows after pos[b] are never read.
+ *   pos       device int32[B], 4-byte aligned: the query's position per batch
+ *             entry. A position outside [0, T_cap) cannot be reported from the
+ *             device: that entry's out and lse are written as NaN.
+ *   alpha, window, pattern  as for fsa_forward_ex.
+ *   out       device float [B][H][D], written; lse device float [B][H], written.
+ * The query attends exactly what row pos[b] of fsa_forward attends. Returns
+ * FSA_ERR_INVALID_ARG for a null or misaligned pointer, T_cap < 1, a bad alpha,
+ * window or pattern; FSA_ERR_UNSUPPORTED as fsa_forward.
+ */
+int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
+               int dtype, int B, int H, int T_cap, int D, const int32_t* pos,
+               float alpha, int window, int pattern, float* out, float* lse,
+               void* stream);
+
 /* fsa_status_string -- static text for a status code. */
 const char* fsa_status_string(int status);
 

@@ -404,6 +404,27 @@ int fsa_backward(const void* q, const void* k, const void* v,
                          workspace_bytes, stream);
 }
 
+int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
+               int dtype, int B, int H, int T_cap, int D, const int32_t* pos,
+               float alpha, int window, int pattern, float* out, float* lse,
+               void* stream) {
+  if (!pattern_ok(pattern) || T_cap < 1) return FSA_ERR_INVALID_ARG;
+  int st = check_shape(dtype, B, H, T_cap, D, alpha, window);
+  if (st != FSA_OK) return st;
+  if (static_cast<long long>(B) * H == 0) return FSA_OK;
+  if (!q || !k_cache || !v_cache || !pos || !out || !lse)
+    return FSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out) || (reinterpret_cast<uintptr_t>(pos) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return FSA_ERR_INVALID_ARG;
+  Taps taps;
+  build_taps(pattern, alpha, window, &taps);
+  return hip_status(launch_decode(q, k_cache, v_cache, dtype, pos, B, H, T_cap,
+                                  D, window, taps, out, lse,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 const char* fsa_status_string(int status) {
   switch (status) {
     case FSA_OK: return "ok";

@@ -57,6 +57,12 @@ size_t bwd_partials_used(const Problem& pr, int dtype);
 hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
                                 hipStream_t s);
 
+// decoding step (fsa_decode.hip): one query per (b, h) at position pos[b]
+// against rows 0..pos[b] of the cached slabs [B][H][Tcap][D]
+hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype,
+                         const int* pos, int B, int H, int Tcap, int D, int W,
+                         const Taps& taps, float* out, float* lse, hipStream_t s);
+
 // lane-per-row kernels (fsa_vec.hip)
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,

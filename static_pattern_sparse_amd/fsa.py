@@ -43,8 +43,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsa.so")
 EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_offsets_ex", "fsa_forward",
            "fsa_forward_ex", "fsa_backward_workspace_size", "fsa_backward",
            "fsa_backward_ex", "fsa_backward_dq", "fsa_backward_dq_ex",
-           "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_status_string",
-           "fsa_last_hip_error")
+           "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_decode",
+           "fsa_status_string", "fsa_last_hip_error")
 
 _lib = None
 
@@ -97,6 +97,9 @@ def lib():
         ex = getattr(L, name + "_ex")
         ex.argtypes = base[:12] + [i32] + base[12:]
         ex.restype = i32
+    L.fsa_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, i32,
+                             i32, vp, vp, vp]
+    L.fsa_decode.restype = i32
     L.fsa_status_string.argtypes = [i32]
     L.fsa_status_string.restype = ctypes.c_char_p
     L.fsa_last_hip_error.argtypes = []
@@ -241,3 +244,30 @@ def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, dalpha,
                                  _ptr(dalpha), _ptr(workspace),
                                  _ws_bytes(workspace), _stream(stream))
     _check("fsa_backward_dkdv", st)
+
+
+def fsa_decode(q, k_cache, v_cache, pos, alpha, window, out=None, lse=None,
+               stream=None, pattern=FSA_PATTERN_FIB):
+    """One decoding step: out [B,H,D] fp32 and lse [B,H] fp32 of the queries
+    q [B,H,D] at positions pos (int32 [B] on the device) against the caches
+    [B,H,T_cap,D]."""
+    import torch
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("expected q [B, H, D] and caches [B, H, T_cap, D]")
+    B, H, T_cap, D = (int(s) for s in k_cache.shape)
+    if tuple(q.shape) != (B, H, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("q, k_cache, v_cache shapes disagree")
+    for x in (q, k_cache, v_cache):
+        if not x.is_cuda or not x.is_contiguous() or x.dtype != q.dtype:
+            raise ValueError("q and the caches must be contiguous device tensors of one dtype")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,) or not pos.is_cuda:
+        raise ValueError("pos must be an int32 device tensor of shape [B]")
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    st = lib().fsa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
+                          B, H, T_cap, D, _ptr(pos), float(alpha), int(window),
+                          int(pattern), _ptr(out), _ptr(lse), _stream(stream))
+    _check("fsa_decode", st)
+    return out, lse

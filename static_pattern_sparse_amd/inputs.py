@@ -61,7 +61,12 @@ WORKLOADS = {w.name: w for w in [
              "linear", (12,), 16, 10000.0, True),
     Workload("linear16_bf16_b1h16t65536d128_w12", 5, 1, 16, 65536, 128,
              "bf16", "linear", (12,), 16, 500000.0, True),
+    # decoding step: one query per (b, h) against caches of 4096 rows (the
+    # evaluation length); four distinct layer caches serve the 16 layers
+    Workload("decode16_bf16_b8h8t4096d64_w12", 6, 8, 8, 4096, 64, "bf16",
+             "linear", (12,), 16, 10000.0, False),
 ]}
+DECODE_CACHES = 4
 
 
 def _rng(workload_id: int, layer: int, tensor: str) -> np.random.Generator:
@@ -137,3 +142,36 @@ def to_device(x: np.ndarray, dtype: str, device="cuda"):
         bits = bf16_bits(x).view(np.int16)
         return torch.from_numpy(bits).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def decode_positions(B: int, T: int) -> np.ndarray:
+    """Query position per batch entry of a decoding step: the last row of the
+    cache for entry 0, then 61 rows earlier per entry (sequences of different
+    lengths in one batch)."""
+    return np.array([max(0, T - 1 - 61 * b) for b in range(B)], dtype=np.int32)
+
+
+def make_decode_inputs(B, H, T, D, dtype, workload_id, layer, positions,
+                       rope_base=10000.0):
+    """One decoding step: caches k, v [B, H, T, D] (k post-RoPE at positions
+    0..T-1, as make_tensor), queries q [B, H, D] drawn N(0, 1) and rotated to
+    position pos[b] (tensor id of q), and pos [B] int32."""
+    pos = np.asarray(positions, dtype=np.int32)
+    k = make_tensor(B, H, T, D, dtype, workload_id, layer, "k", rope_base)
+    v = make_tensor(B, H, T, D, dtype, workload_id, layer, "v", None)
+    cos, sin = rope_tables(T, D, rope_base)
+    rng = _rng(workload_id, layer, "q")
+    q = np.empty((B, H, D), dtype=np.float32)
+    for b in range(B):
+        x = _rope(rng.standard_normal((H, D)), cos[pos[b]], sin[pos[b]])
+        x32 = x.astype(np.float32)
+        q[b] = round_to_bf16(x32) if dtype == "bf16" else x32
+    return {"q": q, "k": k, "v": v, "pos": pos}
+
+
+def decode_inputs(w: Workload, layer: int):
+    """The decoding workload's inputs for one layer (caches cycle over
+    DECODE_CACHES layers)."""
+    return make_decode_inputs(w.B, w.H, w.T, w.D, w.dtype, w.workload_id,
+                              layer % DECODE_CACHES, decode_positions(w.B, w.T),
+                              w.rope_base)

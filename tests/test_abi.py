@@ -179,3 +179,30 @@ def test_pattern_validation_codes():
     for p in F.PATTERNS.values():
         assert lib.fsa_forward_ex(*args[:-1], 0, p, ctypes.c_void_p(FAKE),
                                   ctypes.c_void_p(FAKE), None) == F.FSA_ERR_INVALID_ARG
+
+
+def _dec(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, B=2, H=3, T=64, D=64, pos=FAKE,
+             alpha=1.0, W=4, pattern=0, out=FAKE, lse=FAKE)
+    a.update(kw)
+    ptr = ("q", "k", "v", "pos", "out", "lse")
+    order = ("q", "k", "v", "dtype", "B", "H", "T", "D", "pos", "alpha", "W",
+             "pattern", "out", "lse")
+    return F.lib().fsa_decode(*(ctypes.c_void_p(a[n]) if n in ptr else a[n]
+                                for n in order), None)
+
+
+def test_decode_validation_codes():
+    assert _dec(alpha=1.6) == F.FSA_ERR_INVALID_ARG
+    assert _dec(W=0) == F.FSA_ERR_INVALID_ARG
+    assert _dec(T=0) == F.FSA_ERR_INVALID_ARG               # empty cache
+    assert _dec(pattern=4) == F.FSA_ERR_INVALID_ARG
+    assert _dec(pos=0) == F.FSA_ERR_INVALID_ARG
+    assert _dec(pos=FAKE + 2) == F.FSA_ERR_INVALID_ARG      # misaligned int32
+    assert _dec(q=FAKE + 8) == F.FSA_ERR_INVALID_ARG
+    assert _dec(lse=0) == F.FSA_ERR_INVALID_ARG
+    assert _dec(D=96) == F.FSA_ERR_UNSUPPORTED
+    assert _dec(dtype=7) == F.FSA_ERR_UNSUPPORTED
+    assert _dec(B=300, H=300) == F.FSA_ERR_UNSUPPORTED
+    # no query at all is a no-op
+    assert _dec(B=0, q=0, k=0, v=0, pos=0, out=0, lse=0) == F.FSA_OK

@@ -42,3 +42,20 @@ def test_workload_table_shapes():
     w = I.WORKLOADS["linear16_bf16_b1h16t65536d128_w12"]
     assert (w.B, w.H, w.T, w.D, w.rope_base) == (1, 16, 65536, 128, 500000.0)
     assert len({x.workload_id for x in I.WORKLOADS.values()}) == len(I.WORKLOADS)
+
+
+def test_decode_inputs_share_the_sequence_generator():
+    """A decoding step's caches are the sequence workload's k and v for the
+    same seeds; the query is a rotated N(0,1) row (rotation keeps its norm)."""
+    pos = I.decode_positions(3, 200)
+    assert list(pos) == [199, 138, 77]
+    x = I.make_decode_inputs(3, 2, 200, 64, "f32", 9, 1, pos)
+    seq = I.make_inputs(3, 2, 200, 64, "f32", 9, 1, with_dout=False)
+    assert np.array_equal(x["k"], seq["k"]) and np.array_equal(x["v"], seq["v"])
+    assert x["q"].shape == (3, 2, 64) and x["pos"].dtype == np.int32
+    raw = I._rng(9, 1, "q").standard_normal((2, 64))      # entry 0's draw
+    np.testing.assert_allclose(np.linalg.norm(x["q"][0], axis=1),
+                               np.linalg.norm(raw, axis=1), rtol=1e-6)
+    xb = I.make_decode_inputs(2, 1, 50, 64, "bf16", 9, 1, [49, 0])
+    for t in (xb["q"], xb["k"], xb["v"]):
+        assert np.array_equal(t, I.round_to_bf16(t))       # bf16-exact
