@@ -59,32 +59,34 @@ KERNEL_SOURCES = [os.path.join(ROOT, "static_pattern_sparse_amd", "csrc", n)
                   for n in ("fsa_vec.hip", "fsa_mfma.hip")]
 
 
-def stage_bytes(D, in_bytes):
+def stage_bytes(D, in_bytes, out_bytes=4):
     """Algorithmic HBM bytes per token-head of every kernel: each tensor the
     kernel must read or write, once."""
     row_in = D * in_bytes
     return {
-        "fwd": 3 * row_in + 4 * D + 4,                 # q k v -> out lse
+        "fwd": 3 * row_in + out_bytes * D + 4,         # q k v -> out lse
         "bwd_dq": 4 * row_in + 4 + 4 * D + 4,          # q k v dout lse -> dq delta
         "bwd_dkdv": 4 * row_in + 8 + 8 * D,            # q k v dout lse delta -> dk dv dalpha
     }
 
 
-def algo_bytes(D, in_bytes):
+def algo_bytes(D, in_bytes, out_bytes=4):
     """Algorithmic bytes per token-head of the forward and of the backward as
     a whole (each input read once, each output written once)."""
     row_in = D * in_bytes
-    return {"fwd": 3 * row_in + 4 * D + 4,
+    return {"fwd": 3 * row_in + out_bytes * D + 4,
             "bwd": 4 * row_in + 4 + 12 * D}
 
 
 class Stack:
     """Device buffers of every layer of one workload."""
 
-    def __init__(self, wl, window, layers, torch, F, I, pattern="fib"):
+    def __init__(self, wl, window, layers, torch, F, I, pattern="fib", out_bf16=False):
         self.torch, self.F = torch, F
         self.wl, self.W, self.layers = wl, window, layers
         self.pattern = F.PATTERNS[pattern]
+        self.out_bytes = 2 if out_bf16 else 4
+        out_dt = torch.bfloat16 if out_bf16 else torch.float32
         kind = {"linear": F.FSA_SCHEDULE_LINEAR, "coprime": F.FSA_SCHEDULE_COPRIME,
                 "fixed": F.FSA_SCHEDULE_FIXED}[wl.schedule]
         self.alphas = F.fsa_schedule(kind, wl.layers)
@@ -96,7 +98,8 @@ class Stack:
             x = I.workload_inputs(wl, l)
             t = {n: I.to_device(x[n], wl.dtype) for n in ("q", "k", "v", "dout")}
             f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
-            t.update(out=f32(B, H, T, D), lse=f32(B, H, T), dq=f32(B, H, T, D),
+            t.update(out=torch.empty((B, H, T, D), dtype=out_dt, device=dev),
+                     lse=f32(B, H, T), dq=f32(B, H, T, D),
                      dk=f32(B, H, T, D), dv=f32(B, H, T, D), dalpha=f32(1),
                      ws=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev))
             self.L.append(t)
@@ -118,8 +121,9 @@ class Stack:
             nws = t["ws"].numel()
             a = f32(float(self.alphas[l]))
             pt = self.pattern
+            pf = pt | (F.FSA_OUT_BF16 if self.out_bytes == 2 else 0)
             fwd.append((lib.fsa_forward_ex, (p["q"], p["k"], p["v"], dt, B, H, T, D, a,
-                                             self.W, pt, p["out"], p["lse"], stream)))
+                                             self.W, pf, p["out"], p["lse"], stream)))
             dq.append((lib.fsa_backward_dq_ex, (p["q"], p["k"], p["v"], p["dout"],
                                                 p["lse"], dt, B, H, T, D, a, self.W, pt,
                                                 p["dq"], p["ws"], nws, stream)))
@@ -272,8 +276,8 @@ def summarise(stack, ms_step, per_ms):
     wl = stack.wl
     th = wl.B * wl.H * wl.T                      # token-heads per layer call
     in_b = 2 if wl.dtype == "bf16" else 4
-    sb = stage_bytes(wl.D, in_b)
-    ab = algo_bytes(wl.D, in_b)
+    sb = stage_bytes(wl.D, in_b, stack.out_bytes)
+    ab = algo_bytes(wl.D, in_b, stack.out_bytes)
     kernels = {}
     for n, ms in per_ms.items():
         k = {"mean_us": round(ms * 1e3, 3)}
@@ -375,6 +379,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-t4096", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--out-bf16", action="store_true",
+                    help="the forward writes out in bf16 (FSA_OUT_BF16)")
     ap.add_argument("--pattern", default="fib",
                     choices=["fib", "fib-round", "pow2", "pow2-round"],
                     help="tap pattern: Fibonacci or power-of-two base, "
@@ -406,7 +412,7 @@ def main():
         torch.cuda.empty_cache()
 
     wl = I.WORKLOADS["linear16_bwd_bf16_b8h8t1024d64_w12"]
-    stack = Stack(wl, 12, args.layers, torch, F, I, args.pattern)
+    stack = Stack(wl, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
     print(f"[bench] {wl.name}: {args.layers} layers resident", file=sys.stderr, flush=True)
     ms_step, per_ms, counts = time_stack(stack, args.steps, args.warmup, torch)
     value, kernels, frac = summarise(stack, ms_step, per_ms)
@@ -416,7 +422,8 @@ def main():
     th = wl.B * wl.H * wl.T
     achieved = kernels[dom]["gbs"]
     # the committed counter summaries were taken with the Fibonacci table
-    traffic = load_traffic(dom, th) if args.pattern == "fib" else None
+    traffic = (load_traffic(dom, th)
+               if args.pattern == "fib" and not args.out_bf16 else None)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -431,7 +438,9 @@ def main():
         "data": "synthetic (seeded N(0,1) post-RoPE q, k; v; dout)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "D": wl.D,
                    "W": 12, "layers": args.layers, "schedule": wl.schedule,
-                   "pattern": args.pattern, "pass": "forward+backward"},
+                   "pattern": args.pattern,
+                   "out_dtype": "bf16" if args.out_bf16 else "f32",
+                   "pass": "forward+backward"},
         "roofline": roofline,
         "hbm_frac": frac,
         "kernels": kernels,
@@ -442,7 +451,7 @@ def main():
 
     if not args.skip_t4096:
         wl2 = I.WORKLOADS["coprime16_bf16_b4h8t4096d64_w6-12"]
-        st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern)
+        st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
         print(f"[bench] {wl2.name} W=12 resident", file=sys.stderr, flush=True)
         ms2, per2, _ = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
         v2, k2, f2 = summarise(st2, ms2, per2)

@@ -100,6 +100,14 @@ extern "C" {
 #define FSA_PATTERN_FIB (FSA_BASE_FIBONACCI | FSA_MODE_LERP)
 
 /*
+ * Output option, or-ed into the same argument of fsa_forward_ex and
+ * fsa_decode: `out` holds bf16 (round to nearest even from the fp32 result)
+ * instead of fp32, half the bytes written. lse stays fp32. The backward calls
+ * ignore the bit (they do not take `out`).
+ */
+#define FSA_OUT_BF16 4
+
+/*
  * fsa_schedule -- per-layer alpha table, host only.
  *   kind        FSA_SCHEDULE_*.
  *   num_layers  L >= 1.
@@ -200,14 +208,15 @@ int fsa_backward_dkdv(const void* q, const void* k, const void* v,
                       size_t workspace_bytes, void* stream);
 
 /*
- * _ex variants: the same calls with a tap pattern (FSA_BASE_* | FSA_MODE_*)
- * after `window`; arguments, layouts and errors as above, plus
- * FSA_ERR_INVALID_ARG for an unknown pattern. In FSA_MODE_ROUND dalpha is
- * written as 0.
+ * _ex variants: the same calls with a tap pattern (FSA_BASE_* | FSA_MODE_*,
+ * and FSA_OUT_BF16 for fsa_forward_ex) after `window`; arguments, layouts and
+ * errors as above, plus FSA_ERR_INVALID_ARG for an unknown bit. In
+ * FSA_MODE_ROUND dalpha is written as 0. fsa_forward_ex's `out` is float
+ * [B][H][T][D], or bf16 bits (uint16) [B][H][T][D] with FSA_OUT_BF16.
  */
 int fsa_forward_ex(const void* q, const void* k, const void* v, int dtype,
                    int B, int H, int T, int D, float alpha, int window,
-                   int pattern, float* out, float* lse, void* stream);
+                   int pattern, void* out, float* lse, void* stream);
 int fsa_backward_ex(const void* q, const void* k, const void* v,
                     const void* dout, const float* lse, int dtype, int B, int H,
                     int T, int D, float alpha, int window, int pattern,
@@ -239,15 +248,16 @@ int fsa_backward_dkdv_ex(const void* q, const void* k, const void* v,
  *   pos       device int32[B], 4-byte aligned: the query's position per batch
  *             entry. A position outside [0, T_cap) cannot be reported from the
  *             device: that entry's out and lse are written as NaN.
- *   alpha, window, pattern  as for fsa_forward_ex.
- *   out       device float [B][H][D], written; lse device float [B][H], written.
+ *   alpha, window, pattern  as for fsa_forward_ex (FSA_OUT_BF16 included).
+ *   out       device float [B][H][D] (bf16 bits with FSA_OUT_BF16), written;
+ *   lse       device float [B][H], written.
  * The query attends exactly what row pos[b] of fsa_forward attends. Returns
  * FSA_ERR_INVALID_ARG for a null or misaligned pointer, T_cap < 1, a bad alpha,
  * window or pattern; FSA_ERR_UNSUPPORTED as fsa_forward.
  */
 int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
                int dtype, int B, int H, int T_cap, int D, const int32_t* pos,
-               float alpha, int window, int pattern, float* out, float* lse,
+               float alpha, int window, int pattern, void* out, float* lse,
                void* stream);
 
 /* fsa_status_string -- static text for a status code. */

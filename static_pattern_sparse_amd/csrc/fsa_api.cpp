@@ -40,7 +40,7 @@ const int* base_list(int pattern, int* n) {
 }
 
 bool pattern_ok(int pattern) {
-  return (pattern & ~(FSA_BASE_MASK | FSA_MODE_MASK)) == 0 &&
+  return (pattern & ~(FSA_BASE_MASK | FSA_MODE_MASK | FSA_OUT_BF16)) == 0 &&
          (pattern & FSA_BASE_MASK) <= FSA_BASE_POW2;
 }
 
@@ -194,10 +194,10 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
 // tile kernels; fp32 inputs and wider windows take the lane-per-row kernels.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
-                          float* out, float* lse, hipStream_t s) {
+                          void* out, bool out_bf16, float* lse, hipStream_t s) {
   if (mfma_supported(pr, dtype))
-    return launch_fwd_mfma(q, k, v, pr, taps, out, lse, s);
-  return launch_fwd_vec(q, k, v, dtype, pr, taps, out, lse, s);
+    return launch_fwd_mfma(q, k, v, pr, taps, out, out_bf16, lse, s);
+  return launch_fwd_vec(q, k, v, dtype, pr, taps, out, out_bf16, lse, s);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
@@ -291,7 +291,7 @@ int fsa_offsets(float alpha, int window, int32_t* c_out, float* t_out,
 
 int fsa_forward_ex(const void* q, const void* k, const void* v, int dtype,
                    int B, int H, int T, int D, float alpha, int window,
-                   int pattern, float* out, float* lse, void* stream) {
+                   int pattern, void* out, float* lse, void* stream) {
   if (!pattern_ok(pattern)) return FSA_ERR_INVALID_ARG;
   int st = check_shape(dtype, B, H, T, D, alpha, window);
   if (st != FSA_OK) return st;
@@ -303,7 +303,8 @@ int fsa_forward_ex(const void* q, const void* k, const void* v, int dtype,
   Taps taps;
   build_taps(pattern, alpha, window, &taps);
   const Problem pr = make_problem(B, H, T, D, window);
-  return hip_status(launch_forward(q, k, v, dtype, pr, taps, out, lse,
+  return hip_status(launch_forward(q, k, v, dtype, pr, taps, out,
+                                   (pattern & FSA_OUT_BF16) != 0, lse,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -406,7 +407,7 @@ int fsa_backward(const void* q, const void* k, const void* v,
 
 int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
                int dtype, int B, int H, int T_cap, int D, const int32_t* pos,
-               float alpha, int window, int pattern, float* out, float* lse,
+               float alpha, int window, int pattern, void* out, float* lse,
                void* stream) {
   if (!pattern_ok(pattern) || T_cap < 1) return FSA_ERR_INVALID_ARG;
   int st = check_shape(dtype, B, H, T_cap, D, alpha, window);
@@ -421,7 +422,8 @@ int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
   Taps taps;
   build_taps(pattern, alpha, window, &taps);
   return hip_status(launch_decode(q, k_cache, v_cache, dtype, pos, B, H, T_cap,
-                                  D, window, taps, out, lse,
+                                  D, window, taps, out,
+                                  (pattern & FSA_OUT_BF16) != 0, lse,
                                   static_cast<hipStream_t>(stream)));
 }
 

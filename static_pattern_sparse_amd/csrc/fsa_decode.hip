@@ -132,11 +132,21 @@ __device__ __forceinline__ void fetch(const Tin* K, const Tin* V, int D, const E
   load_chunk<C>(V + r1, v1);
 }
 
-template <typename Tin, int D>
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void put(float* o, float x) { *o = x; }
+// bf16 bits, round to nearest even
+__device__ __forceinline__ void put(uint16_t* o, float x) {
+  *o = static_cast<uint16_t>(
+      __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, 0.f}, bf16x2)));
+}
+
+template <typename Tin, int D, typename OutT>
 __global__ __launch_bounds__(kDecBlock) void decode_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ kc,
     const Tin* __restrict__ vc, const int* __restrict__ pos, int H, int Tcap,
-    int W, float c2, Taps taps, float* __restrict__ out, float* __restrict__ lse) {
+    int W, float c2, Taps taps, OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int C = D / 16;
   constexpr float kLn2 = 0.6931471805599453f;
   __shared__ float s_m[kGroups], s_l[kGroups];
@@ -145,9 +155,9 @@ __global__ __launch_bounds__(kDecBlock) void decode_kernel(
   const int grp = tid >> 4, e = tid & 15;
   const int bh = blockIdx.x;
   const int i = pos[bh / H];
-  float* o = out + static_cast<size_t>(bh) * D;
+  OutT* o = out + static_cast<size_t>(bh) * D;
   if (i < 0 || i >= Tcap) {              // the same for the whole workgroup
-    if (tid < D) o[tid] = NAN;
+    if (tid < D) put(o + tid, NAN);
     if (tid == 0) lse[bh] = NAN;
     return;
   }
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(kDecBlock) void decode_kernel(
       L = fmaf(s_l[g], f, L);
       od = fmaf(s_acc[g][tid], f, od);
     }
-    o[tid] = od / L;
+    put(o + tid, od / L);
     if (tid == 0) lse[bh] = (M + log2f(L)) * kLn2;
   }
 }
@@ -244,11 +254,19 @@ __global__ __launch_bounds__(kDecBlock) void decode_kernel(
 template <typename Tin, int D>
 hipError_t decode_typed(const void* q, const void* k, const void* v,
                         const int* pos, int B, int H, int Tcap, int W,
-                        const Taps& taps, float* out, float* lse, hipStream_t s) {
+                        const Taps& taps, void* out, bool out_bf16, float* lse,
+                        hipStream_t s) {
   const float c2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-  hipLaunchKernelGGL((decode_kernel<Tin, D>), dim3(B * H), dim3(kDecBlock), 0, s,
-                     static_cast<const Tin*>(q), static_cast<const Tin*>(k),
-                     static_cast<const Tin*>(v), pos, H, Tcap, W, c2, taps, out, lse);
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_kernel<Tin, D, uint16_t>), dim3(B * H), dim3(kDecBlock), 0, s,
+                       static_cast<const Tin*>(q), static_cast<const Tin*>(k),
+                       static_cast<const Tin*>(v), pos, H, Tcap, W, c2, taps,
+                       static_cast<uint16_t*>(out), lse);
+  else
+    hipLaunchKernelGGL((decode_kernel<Tin, D, float>), dim3(B * H), dim3(kDecBlock), 0, s,
+                       static_cast<const Tin*>(q), static_cast<const Tin*>(k),
+                       static_cast<const Tin*>(v), pos, H, Tcap, W, c2, taps,
+                       static_cast<float*>(out), lse);
   return hipGetLastError();
 }
 
@@ -256,12 +274,13 @@ hipError_t decode_typed(const void* q, const void* k, const void* v,
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype,
                          const int* pos, int B, int H, int Tcap, int D, int W,
-                         const Taps& taps, float* out, float* lse, hipStream_t s) {
+                         const Taps& taps, void* out, bool out_bf16, float* lse,
+                         hipStream_t s) {
   if (dtype == FSA_DTYPE_F32)
-    return D == 64 ? decode_typed<float, 64>(q, k, v, pos, B, H, Tcap, W, taps, out, lse, s)
-                   : decode_typed<float, 128>(q, k, v, pos, B, H, Tcap, W, taps, out, lse, s);
-  return D == 64 ? decode_typed<uint16_t, 64>(q, k, v, pos, B, H, Tcap, W, taps, out, lse, s)
-                 : decode_typed<uint16_t, 128>(q, k, v, pos, B, H, Tcap, W, taps, out, lse, s);
+    return D == 64 ? decode_typed<float, 64>(q, k, v, pos, B, H, Tcap, W, taps, out, out_bf16, lse, s)
+                   : decode_typed<float, 128>(q, k, v, pos, B, H, Tcap, W, taps, out, out_bf16, lse, s);
+  return D == 64 ? decode_typed<uint16_t, 64>(q, k, v, pos, B, H, Tcap, W, taps, out, out_bf16, lse, s)
+                 : decode_typed<uint16_t, 128>(q, k, v, pos, B, H, Tcap, W, taps, out, out_bf16, lse, s);
 }
 
 }  // namespace fsa

@@ -38,10 +38,11 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype);
 
 // Launchers; each returns the hipError_t of its launch. The kernel family is
 // chosen from dtype: fp32 inputs use the lane-per-row kernels, bf16 inputs the
-// MFMA tile kernels.
+// MFMA tile kernels. `out` is fp32, or bf16 (round to nearest even) when
+// out_bf16.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
-                          float* out, float* lse, hipStream_t s);
+                          void* out, bool out_bf16, float* lse, hipStream_t s);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, int dtype,
                          const Problem& pr, const Taps& taps, float* dq,
@@ -61,12 +62,13 @@ hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
 // against rows 0..pos[b] of the cached slabs [B][H][Tcap][D]
 hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype,
                          const int* pos, int B, int H, int Tcap, int D, int W,
-                         const Taps& taps, float* out, float* lse, hipStream_t s);
+                         const Taps& taps, void* out, bool out_bf16, float* lse,
+                         hipStream_t s);
 
 // lane-per-row kernels (fsa_vec.hip)
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
-                          float* out, float* lse, hipStream_t s);
+                          void* out, bool out_bf16, float* lse, hipStream_t s);
 hipError_t launch_bwd_dq_vec(const void* q, const void* k, const void* v,
                              const void* dout, const float* lse, int dtype,
                              const Problem& pr, const Taps& taps, float* dq,
@@ -81,8 +83,8 @@ size_t bwd_partials_used_vec(const Problem& pr);
 // MFMA tile kernels (fsa_mfma.hip): bf16 inputs, D in {64, 128}, W <= 33
 bool mfma_supported(const Problem& pr, int dtype);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
-                           const Problem& pr, const Taps& taps, float* out,
-                           float* lse, hipStream_t s);
+                           const Problem& pr, const Taps& taps, void* out,
+                           bool out_bf16, float* lse, hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               const void* dout, const float* lse,
                               const Problem& pr, const Taps& taps, float* dq,

@@ -472,31 +472,66 @@ __device__ __forceinline__ float tap_part(const f32x4& s, const LaneSel& ls, flo
 }
 
 
-// Store a 16-row fp32 result tile held in the C layout of the products over
-// rows (lane (g, n): row n, columns 16mb + 4g .. +3) through LDS, so that each
-// non-temporal store instruction writes whole rows (1 KB: 4 rows at D = 64,
-// 2 at D = 128). Stored piecewise from the C layout, the non-temporal writes
-// cover half cache lines and are not merged (measured HBM writes 1.3-1.4x the
-// bytes). Row r of the tile goes to dst + r*D when row_ok(r); `buf` needs
-// 16 * (4D + 16) bytes and must no longer be read by this wavefront.
-template <int D, typename RowOk>
-__device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, float* dst, int lane,
-                                           RowOk row_ok) {
+// Store a 16-row result tile held in the C layout of the products over rows
+// (lane (g, n): row n, columns 16mb + 4g .. +3) through LDS, so that each
+// non-temporal store instruction writes whole rows (1 KB: 4 rows of fp32 at
+// D = 64, 2 at D = 128; bf16 rows take half). Stored piecewise from the C
+// layout, the non-temporal writes cover half cache lines and are not merged
+// (measured HBM writes 1.3-1.4x the bytes). Row r of the tile goes to
+// dst + r*D when row_ok(r); `buf` needs 16 * (4D + 16) bytes and must no
+// longer be read by this wavefront.
+template <int D>
+__device__ __forceinline__ void tile_to_lds(lds_char* buf, const f32x4* acc, int lane) {
   constexpr int kPitch = 4 * D + 16;                   // padded row (bank spread)
-  constexpr int kLanesPerRow = D / 4;                  // float4 per row
-  constexpr int kRowsPerStore = 64 / kLanesPerRow;
   const int n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb)
     *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(buf + n * kPitch + (16 * mb + 4 * g) * 4) = acc[mb];
   __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, typename RowOk>
+__device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, float* dst, int lane,
+                                           RowOk row_ok) {
+  constexpr int kPitch = 4 * D + 16;
+  constexpr int kLanesPerRow = D / 4;                  // float4 per row
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  tile_to_lds<D>(buf, acc, lane);
   const int c = lane % kLanesPerRow;
 #pragma unroll
   for (int it = 0; it < 16 / kRowsPerStore; ++it) {
     const int r = kRowsPerStore * it + lane / kLanesPerRow;
     const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(buf + r * kPitch + 16 * c);
     if (row_ok(r)) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(dst + static_cast<size_t>(r) * D + 4 * c));
+  }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats as packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// The same tile rounded to bf16 (dst holds bf16 bits): 8 elements per lane.
+template <int D, typename RowOk>
+__device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, uint16_t* dst, int lane,
+                                           RowOk row_ok) {
+  constexpr int kPitch = 4 * D + 16;
+  constexpr int kLanesPerRow = D / 8;                  // 16 bytes of bf16 per lane
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  tile_to_lds<D>(buf, acc, lane);
+  const int c = lane % kLanesPerRow;
+#pragma unroll
+  for (int it = 0; it < 16 / kRowsPerStore; ++it) {
+    const int r = kRowsPerStore * it + lane / kLanesPerRow;
+    const auto* src = reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(buf + r * kPitch + 32 * c);
+    const f32x4 x0 = src[0], x1 = src[1];
+    const u32x4 y{pack_bf16(x0[0], x0[1]), pack_bf16(x0[2], x0[3]),
+                  pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
+    if (row_ok(r)) __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(dst + static_cast<size_t>(r) * D + 8 * c));
   }
 }
 
@@ -513,11 +548,11 @@ __device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, floa
 // query n's score, and m is raised only when a score passes it by more than
 // 2^kLazy (weights up to 2^kLazy are summed as they are): the rescale of the
 // accumulators is then rare, and l, the output and lse stay exact.
-template <int D>
+template <int D, typename OutT>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Problem pr, Taps taps, int n_tiles,
-    float* __restrict__ out, float* __restrict__ lse) {
+    OutT* __restrict__ out, float* __restrict__ lse) {
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;         // K_x K_y V_x V_y
   constexpr float kLog2e = 1.4426950408889634f;
@@ -1080,19 +1115,30 @@ bool mfma_supported(const Problem& pr, int dtype) {
 }
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
-                           const Problem& pr, const Taps& taps, float* out,
-                           float* lse, hipStream_t s) {
+                           const Problem& pr, const Taps& taps, void* out,
+                           bool out_bf16, float* lse, hipStream_t s) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
-  if (pr.D == 64)
-    hipLaunchKernelGGL(fwd_mfma_kernel<64>, grid, dim3(64), 0, s, qq, kk, vv, pr,
-                       taps, n_tiles, out, lse);
-  else
-    hipLaunchKernelGGL(fwd_mfma_kernel<128>, grid, dim3(64), 0, s, qq, kk, vv, pr,
-                       taps, n_tiles, out, lse);
+  auto* of = static_cast<float*>(out);
+  auto* ob = static_cast<uint16_t*>(out);
+  if (pr.D == 64) {
+    if (out_bf16)
+      hipLaunchKernelGGL((fwd_mfma_kernel<64, uint16_t>), grid, dim3(64), 0, s, qq, kk, vv, pr,
+                         taps, n_tiles, ob, lse);
+    else
+      hipLaunchKernelGGL((fwd_mfma_kernel<64, float>), grid, dim3(64), 0, s, qq, kk, vv, pr,
+                         taps, n_tiles, of, lse);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((fwd_mfma_kernel<128, uint16_t>), grid, dim3(64), 0, s, qq, kk, vv, pr,
+                         taps, n_tiles, ob, lse);
+    else
+      hipLaunchKernelGGL((fwd_mfma_kernel<128, float>), grid, dim3(64), 0, s, qq, kk, vv, pr,
+                         taps, n_tiles, of, lse);
+  }
   return hipGetLastError();
 }
 

@@ -21,6 +21,30 @@ namespace {
 
 constexpr int kVecBlock = 64;  // one wavefront per workgroup
 
+// ---- result rows: fp32, or bf16 rounded to nearest even --------------------
+template <int D>
+__device__ __forceinline__ void store_row(float* o, const float* acc) {
+#pragma unroll
+  for (int d = 0; d < D; d += 4)
+    *reinterpret_cast<float4*>(o + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+__device__ __forceinline__ void store_row(uint16_t* o, const float* acc) {
+#pragma unroll
+  for (int d = 0; d < D; d += 8) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                              f32x2{acc[d + 2 * e], acc[d + 2 * e + 1]}, bf16x2));
+    *reinterpret_cast<uint4*>(o + d) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // ---- row access, converted to fp32 ----------------------------------------
 __device__ __forceinline__ void load8(const float* p, float* r) {
   const float4 a = reinterpret_cast<const float4*>(p)[0];
@@ -74,10 +98,10 @@ __device__ __forceinline__ void axpy_row(float a, const Tin* p, float* acc) {
 // ---- forward ---------------------------------------------------------------
 // out_i = sum_e softmax(s)_e * value_e over the window entries j = i-w
 // (w < W, j >= 0) and the kept taps with i >= c (rows a = i-c, a+1).
-template <typename Tin, int D>
+template <typename Tin, int D, typename OutT>
 __global__ __launch_bounds__(kVecBlock) void fwd_vec_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k,
-    const Tin* __restrict__ v, Problem pr, Taps taps, float* __restrict__ out,
+    const Tin* __restrict__ v, Problem pr, Taps taps, OutT* __restrict__ out,
     float* __restrict__ lse) {
   const int i = blockIdx.x * kVecBlock + threadIdx.x;
   const int T = pr.T;
@@ -127,10 +151,7 @@ __global__ __launch_bounds__(kVecBlock) void fwd_vec_kernel(
     axpy_row<Tin, D>(p * wl, V + a, acc);
     if (wh != 0.f) axpy_row<Tin, D>(p * wh, V + a + D, acc);
   }
-  float* o = out + base + static_cast<size_t>(i) * D;
-#pragma unroll
-  for (int d = 0; d < D; d += 4)
-    *reinterpret_cast<float4*>(o + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
+  store_row<D>(out + base + static_cast<size_t>(i) * D, acc);
   lse[static_cast<size_t>(blockIdx.y) * T + i] = L;
 }
 
@@ -333,12 +354,17 @@ hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
 namespace {
 template <typename Tin, int D>
 hipError_t fwd_vec_typed(const void* q, const void* k, const void* v,
-                         const Problem& pr, const Taps& taps, float* out,
-                         float* lse, hipStream_t s) {
+                         const Problem& pr, const Taps& taps, void* out,
+                         bool out_bf16, float* lse, hipStream_t s) {
   dim3 grid((pr.T + kVecBlock - 1) / kVecBlock, pr.B * pr.H);
-  hipLaunchKernelGGL((fwd_vec_kernel<Tin, D>), grid, dim3(kVecBlock), 0, s,
-                     static_cast<const Tin*>(q), static_cast<const Tin*>(k),
-                     static_cast<const Tin*>(v), pr, taps, out, lse);
+  if (out_bf16)
+    hipLaunchKernelGGL((fwd_vec_kernel<Tin, D, uint16_t>), grid, dim3(kVecBlock), 0, s,
+                       static_cast<const Tin*>(q), static_cast<const Tin*>(k),
+                       static_cast<const Tin*>(v), pr, taps, static_cast<uint16_t*>(out), lse);
+  else
+    hipLaunchKernelGGL((fwd_vec_kernel<Tin, D, float>), grid, dim3(kVecBlock), 0, s,
+                       static_cast<const Tin*>(q), static_cast<const Tin*>(k),
+                       static_cast<const Tin*>(v), pr, taps, static_cast<float*>(out), lse);
   return hipGetLastError();
 }
 
@@ -372,13 +398,13 @@ hipError_t bwd_dkdv_vec_typed(const void* q, const void* k, const void* v,
 
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
-                          float* out, float* lse, hipStream_t s) {
+                          void* out, bool out_bf16, float* lse, hipStream_t s) {
   if (dtype == FSA_DTYPE_F32) {
-    return pr.D == 64 ? fwd_vec_typed<float, 64>(q, k, v, pr, taps, out, lse, s)
-                      : fwd_vec_typed<float, 128>(q, k, v, pr, taps, out, lse, s);
+    return pr.D == 64 ? fwd_vec_typed<float, 64>(q, k, v, pr, taps, out, out_bf16, lse, s)
+                      : fwd_vec_typed<float, 128>(q, k, v, pr, taps, out, out_bf16, lse, s);
   }
-  return pr.D == 64 ? fwd_vec_typed<uint16_t, 64>(q, k, v, pr, taps, out, lse, s)
-                    : fwd_vec_typed<uint16_t, 128>(q, k, v, pr, taps, out, lse, s);
+  return pr.D == 64 ? fwd_vec_typed<uint16_t, 64>(q, k, v, pr, taps, out, out_bf16, lse, s)
+                    : fwd_vec_typed<uint16_t, 128>(q, k, v, pr, taps, out, out_bf16, lse, s);
 }
 
 size_t bwd_partials_used_vec(const Problem& pr) {

@@ -34,6 +34,7 @@ FSA_BASE_POW2 = 1
 FSA_MODE_LERP = 0
 FSA_MODE_ROUND = 2
 FSA_PATTERN_FIB = FSA_BASE_FIBONACCI | FSA_MODE_LERP
+FSA_OUT_BF16 = 4
 PATTERNS = {"fib": FSA_PATTERN_FIB,
             "fib-round": FSA_BASE_FIBONACCI | FSA_MODE_ROUND,
             "pow2": FSA_BASE_POW2 | FSA_MODE_LERP,
@@ -162,20 +163,36 @@ def _shape(q):
     return tuple(int(s) for s in q.shape)
 
 
+def _out_buffer(out, out_dtype, shape, device, pattern):
+    """The output tensor (fp32 or bf16) and the flags that describe it."""
+    import torch
+    if out is None:
+        dt = torch.float32 if out_dtype is None else out_dtype
+        out = torch.empty(shape, dtype=dt, device=device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    if tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {tuple(shape)} tensor")
+    flags = int(pattern) & ~FSA_OUT_BF16
+    if out.dtype == torch.bfloat16:
+        flags |= FSA_OUT_BF16
+    return out, flags
+
+
 def fsa_forward(q, k, v, alpha, window, out=None, lse=None, stream=None,
-                pattern=FSA_PATTERN_FIB):
-    """out [B,H,T,D] fp32 and lse [B,H,T] fp32 of one layer."""
+                pattern=FSA_PATTERN_FIB, out_dtype=None):
+    """out [B,H,T,D] (fp32, or bf16 with out_dtype=torch.bfloat16 or a bf16
+    `out`) and lse [B,H,T] fp32 of one layer."""
     import torch
     B, H, T, D = _shape(q)
     for x in (k, v):
         if x.shape != q.shape or x.dtype != q.dtype or not x.is_contiguous():
             raise ValueError("q, k, v must share shape, dtype and be contiguous")
-    if out is None:
-        out = torch.empty((B, H, T, D), dtype=torch.float32, device=q.device)
+    out, flags = _out_buffer(out, out_dtype, (B, H, T, D), q.device, pattern)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     st = lib().fsa_forward_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H,
-                              T, D, float(alpha), int(window), int(pattern),
+                              T, D, float(alpha), int(window), flags,
                               _ptr(out), _ptr(lse), _stream(stream))
     _check("fsa_forward", st)
     return out, lse
@@ -247,7 +264,7 @@ def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, dalpha,
 
 
 def fsa_decode(q, k_cache, v_cache, pos, alpha, window, out=None, lse=None,
-               stream=None, pattern=FSA_PATTERN_FIB):
+               stream=None, pattern=FSA_PATTERN_FIB, out_dtype=None):
     """One decoding step: out [B,H,D] fp32 and lse [B,H] fp32 of the queries
     q [B,H,D] at positions pos (int32 [B] on the device) against the caches
     [B,H,T_cap,D]."""
@@ -262,12 +279,11 @@ def fsa_decode(q, k_cache, v_cache, pos, alpha, window, out=None, lse=None,
             raise ValueError("q and the caches must be contiguous device tensors of one dtype")
     if pos.dtype != torch.int32 or tuple(pos.shape) != (B,) or not pos.is_cuda:
         raise ValueError("pos must be an int32 device tensor of shape [B]")
-    if out is None:
-        out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    out, flags = _out_buffer(out, out_dtype, (B, H, D), q.device, pattern)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     st = lib().fsa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
                           B, H, T_cap, D, _ptr(pos), float(alpha), int(window),
-                          int(pattern), _ptr(out), _ptr(lse), _stream(stream))
+                          flags, _ptr(out), _ptr(lse), _stream(stream))
     _check("fsa_decode", st)
     return out, lse

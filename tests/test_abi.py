@@ -161,20 +161,20 @@ def test_offsets_ex_vs_oracle(name, alpha, W):
 
 def test_pattern_validation_codes():
     with pytest.raises(F.FsaError):
-        F.fsa_offsets(1.0, 8, 4)
+        F.fsa_offsets(1.0, 8, 8)
     with pytest.raises(F.FsaError):
         F.fsa_offsets(1.0, 8, -1)
     lib = F.lib()
     args = [ctypes.c_void_p(FAKE)] * 3 + [1, 1, 1, 16, 64, 1.0, 4]
-    for bad in (4, 8, -1):
+    for bad in (8, 16, -1):
         assert lib.fsa_forward_ex(*args, bad, ctypes.c_void_p(FAKE),
                                   ctypes.c_void_p(FAKE), None) == F.FSA_ERR_INVALID_ARG
     bwd = [ctypes.c_void_p(FAKE)] * 5 + [1, 1, 1, 16, 64, 1.0, 4]
     out4 = [ctypes.c_void_p(FAKE)] * 5 + [1 << 20, None]
-    assert lib.fsa_backward_ex(*bwd, 4, *out4) == F.FSA_ERR_INVALID_ARG
-    assert lib.fsa_backward_dq_ex(*bwd, 4, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+    assert lib.fsa_backward_ex(*bwd, 8, *out4) == F.FSA_ERR_INVALID_ARG
+    assert lib.fsa_backward_dq_ex(*bwd, 8, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
                                   1 << 20, None) == F.FSA_ERR_INVALID_ARG
-    assert lib.fsa_backward_dkdv_ex(*bwd, 4, *out4[1:]) == F.FSA_ERR_INVALID_ARG
+    assert lib.fsa_backward_dkdv_ex(*bwd, 8, *out4[1:]) == F.FSA_ERR_INVALID_ARG
     # every valid pattern passes validation up to the first bad argument
     for p in F.PATTERNS.values():
         assert lib.fsa_forward_ex(*args[:-1], 0, p, ctypes.c_void_p(FAKE),
@@ -196,7 +196,7 @@ def test_decode_validation_codes():
     assert _dec(alpha=1.6) == F.FSA_ERR_INVALID_ARG
     assert _dec(W=0) == F.FSA_ERR_INVALID_ARG
     assert _dec(T=0) == F.FSA_ERR_INVALID_ARG               # empty cache
-    assert _dec(pattern=4) == F.FSA_ERR_INVALID_ARG
+    assert _dec(pattern=8) == F.FSA_ERR_INVALID_ARG
     assert _dec(pos=0) == F.FSA_ERR_INVALID_ARG
     assert _dec(pos=FAKE + 2) == F.FSA_ERR_INVALID_ARG      # misaligned int32
     assert _dec(q=FAKE + 8) == F.FSA_ERR_INVALID_ARG

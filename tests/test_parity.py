@@ -308,3 +308,37 @@ def test_workload_long_t65536_sampled(layer):
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
         ref = math.fsum(ex.map(_pool.slab_dalpha, jobs))
     assert abs(float(da.item()) - ref) <= DALPHA_RTOL * abs(ref)
+
+
+# ------------------------------------------------------------------ bf16 output
+BF16_OUT_CASES = [
+    # B, H, T, D, dtype, alpha, W  (tile kernels, then lane-per-row kernels)
+    (2, 2, 700, 64, "bf16", 0.7317, 12),
+    (1, 2, 333, 128, "bf16", 1.2913, 6),
+    (1, 1, 300, 64, "f32", 0.9, 5),
+    (1, 1, 260, 64, "bf16", 0.6333333, 40),
+]
+
+
+@pytest.mark.parametrize("B,H,T,D,dtype,alpha,W", BF16_OUT_CASES)
+def test_forward_bf16_out(B, H, T, D, dtype, alpha, W):
+    """FSA_OUT_BF16: the stored out is the fp32 result rounded to nearest even
+    (bit for bit against the fp32 call), lse unchanged; against the oracle the
+    bound widens by the rounding, 2^-8 |out|."""
+    torch = _torch()
+    from static_pattern_sparse_amd import fsa as F
+    _say("bf16 out", B, H, T, D, dtype, alpha, W)
+    alpha = float(np.float32(alpha))
+    x = _rand_inputs(B, H, T, D, dtype, 6)
+    q, k, v = (I.to_device(x[n], dtype) for n in ("q", "k", "v"))
+    o32, l32 = F.fsa_forward(q, k, v, alpha, W)
+    ob = torch.full((B, H, T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ob, lb = F.fsa_forward(q, k, v, alpha, W, out=ob)
+    torch.cuda.synchronize()
+    assert ob.dtype == torch.bfloat16
+    assert torch.equal(ob, o32.to(torch.bfloat16))
+    assert torch.equal(lb, l32)
+    xd = _f64(x)
+    ro, _ = O.forward(xd["q"], xd["k"], xd["v"], alpha, W)
+    err = np.abs(_np(ob) - ro) - (TOL[dtype] + 2.0 ** -8 * np.abs(ro))
+    assert float(err.max()) <= 0.0

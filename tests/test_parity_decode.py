@@ -142,3 +142,19 @@ def test_workload_decode_t4096():
         _say(w.name, layer)
         x = I.decode_inputs(w, layer)
         check_decode(x, w.dtype, float(alphas[layer]), 12)
+
+
+def test_decode_bf16_out():
+    """FSA_OUT_BF16 in the decoding step: the fp32 result rounded to nearest
+    even, bit for bit."""
+    torch = _torch()
+    from static_pattern_sparse_amd import fsa as F
+    _say("decode bf16 out")
+    x = I.make_decode_inputs(4, 2, 1200, 64, "bf16", 84, 0, [1199, 700, 12, 0])
+    q, k, v = (I.to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    pos = torch.from_numpy(x["pos"]).to("cuda")
+    o32, l32 = F.fsa_decode(q, k, v, pos, 0.8, 12)
+    ob, lb = F.fsa_decode(q, k, v, pos, 0.8, 12, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert ob.dtype == torch.bfloat16
+    assert torch.equal(ob, o32.to(torch.bfloat16)) and torch.equal(lb, l32)
