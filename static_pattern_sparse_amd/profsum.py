@@ -19,12 +19,30 @@ import re
 import sys
 
 
+_TYPES = {"unsigned short": "bf16", "float": "f32"}
+
+
+def kernel_label(full):
+    """Short name of a kernel: its name and template arguments, element types
+    abbreviated (bf16 bits, f32); the forward's default fp32 output is left
+    out, so that fwd_mfma_kernel<64, float> reads fwd_mfma_kernel<64>."""
+    m = re.search(r"(\w+_kernel)(?:<([^<>]*)>)?", full)
+    if not m:
+        return full[:40]
+    name, inner = m.group(1), m.group(2)
+    if not inner:
+        return name
+    args = [a.strip() for a in inner.split(",")]
+    if name == "fwd_mfma_kernel" and args[-1] == "float":
+        args = args[:-1]
+    return name + "<" + ",".join(_TYPES.get(a, a) for a in args) + ">"
+
+
 def summarise(path):
     agg = collections.defaultdict(list)
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            m = re.search(r"(\w+_kernel)(<\d+>)?", r["Kernel_Name"])
-            name = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:40]
+            name = kernel_label(r["Kernel_Name"])
             key = (name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
             agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["%-28s %9s %5s %9s %9s %9s %9s" % ("kernel", "workgroups", "n",
@@ -43,8 +61,7 @@ def _counter_means(path):
     agg = collections.defaultdict(list)
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            m = re.search(r"(\w+_kernel)(<\d+>)?", r["Kernel_Name"])
-            name = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:40]
+            name = kernel_label(r["Kernel_Name"])
             key = (name, int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
             agg[key].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in agg.items()}
