@@ -340,9 +340,10 @@ def _noop(_):
     return os.getpid()
 
 
-def cpu_baseline(wl, window, alphas, layers, pattern="fib"):
+def cpu_baseline(wl, window, alphas, layers, pattern="fib", passes=2):
     """The fp64 oracle (forward + backward of every (b, h) slab) over whole
-    layers of the workload, one layer per worker task."""
+    layers of the workload, one layer per worker task, `passes` times over the
+    step (about 15 s of CPU work in all)."""
     from static_pattern_sparse_amd import inputs as I
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
@@ -358,12 +359,13 @@ def cpu_baseline(wl, window, alphas, layers, pattern="fib"):
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
         list(ex.map(_noop, range(workers * 2)))          # start every worker
         t0 = time.perf_counter()
-        busy = list(ex.map(_oracle_layer, jobs))
+        busy = list(ex.map(_oracle_layer, jobs * passes))
         wall = time.perf_counter() - t0
-    th = layers * wl.B * wl.H * wl.T
+    th = passes * layers * wl.B * wl.H * wl.T
     return {"value": round(th / wall, 1), "unit": "tokens·heads/s",
             "cores": workers, "kind": "oracle",
-            "sample": (f"{layers} layers x {wl.B * wl.H} (b,h) slabs of {wl.name}, "
+            "sample": (f"{passes} passes over {layers} layers x {wl.B * wl.H} (b,h) "
+                       f"slabs of {wl.name}, "
                        f"forward+backward in fp64 numpy, {workers} spawned "
                        f"single-threaded workers; {wall:.1f} s wall, "
                        f"{sum(busy):.1f} s CPU")}
