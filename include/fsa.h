@@ -151,7 +151,9 @@ int fsa_offsets_ex(int pattern, float alpha, int window, int32_t* c_out,
  * [DSFS: Methodology > Architecture and attention]
  *   q, k, v   device [B][H][T][D] of `dtype` (q, k post-RoPE), 16-byte aligned.
  *   dtype     FSA_DTYPE_F32 or FSA_DTYPE_BF16.
- *   B, H, T   >= 0 (a zero product is a no-op); D in {64, 128}.
+ *   B, H, T   >= 0 (a zero product is a no-op); D in {64, 128}. Sizes past
+ *             B*H = 65535 or T*D = 2^29 (the kernels' 32-bit offsets within a
+ *             slab) return FSA_ERR_UNSUPPORTED.
  *   alpha     fp32 in [0.5, 1.5]; window W >= 1 (W >= T gives causal attention).
  *   out       device float [B][H][T][D], written (fp32 for every dtype).
  *   lse       device float [B][H][T], written: log of the softmax denominator

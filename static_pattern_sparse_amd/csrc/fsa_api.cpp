@@ -117,8 +117,13 @@ int check_shape(int dtype, int B, int H, int T, int D, float alpha, int window) 
     return FSA_ERR_INVALID_ARG;
   if (dtype != FSA_DTYPE_F32 && dtype != FSA_DTYPE_BF16) return FSA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return FSA_ERR_UNSUPPORTED;
-  // grid limits: heads on grid.y, 64-bit element offsets inside the kernels
+  // grid limits: heads on grid.y of the lane-per-row kernels, one tile per
+  // workgroup on grid.x of the tile kernels
   if (static_cast<long long>(B) * H > 65535) return FSA_ERR_UNSUPPORTED;
+  if ((static_cast<long long>(T) + 13) / 14 * B * H > 0x7fffffffLL)
+    return FSA_ERR_UNSUPPORTED;
+  // byte offsets within one (b, h) slab are 32-bit in the kernels
+  if (static_cast<long long>(T) * D >= (1LL << 29)) return FSA_ERR_UNSUPPORTED;
   return FSA_OK;
 }
 

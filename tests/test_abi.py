@@ -105,6 +105,8 @@ def test_forward_validation_codes():
     assert _fwd(lse=0) == F.FSA_ERR_INVALID_ARG
     assert _fwd(k=FAKE + 2) == F.FSA_ERR_INVALID_ARG       # misaligned
     assert _fwd(B=300, H=300) == F.FSA_ERR_UNSUPPORTED       # too many heads
+    assert _fwd(T=1 << 23, D=64) == F.FSA_ERR_UNSUPPORTED    # slab past 32-bit offsets
+    assert _fwd(T=1 << 22, D=128) == F.FSA_ERR_UNSUPPORTED
     # an empty problem is a no-op that touches nothing
     assert _fwd(T=0, q=0, k=0, v=0, out=0, lse=0) == F.FSA_OK
     assert _fwd(B=0) == F.FSA_OK
