@@ -28,6 +28,7 @@ counted). The JSON line also carries:
                 they match the current kernel source, else null;
   cpu_baseline  the fp64 oracle on the host cores over the same step;
   t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12;
+  t65536        one layer (forward and backward) at B=1, H=16, T=65536, D=128;
   decode        a decoding step (one new query per (b, h) in each of the 16
                 layers, B=8, H=8, caches of 4096 rows, W=12): time per step,
                 tokens per second and the mean launch time. Four distinct layer
@@ -381,6 +382,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-t4096", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-t65536", action="store_true")
     ap.add_argument("--out-bf16", action="store_true",
                     help="the forward writes out in bf16 (FSA_OUT_BF16)")
     ap.add_argument("--pattern", default="fib",
@@ -460,6 +462,18 @@ def main():
         res["t4096"] = {"workload": wl2.name + " (W=12)", "value": round(v2, 1),
                         "ms_per_step": round(ms2, 4), "hbm_frac": f2, "kernels": k2}
         del st2
+        torch.cuda.empty_cache()
+
+    if not args.skip_t65536:
+        wl4 = I.WORKLOADS["linear16_bf16_b1h16t65536d128_w12"]
+        st4 = Stack(wl4, 12, 1, torch, F, I, args.pattern, args.out_bf16)
+        print(f"[bench] {wl4.name} (one layer) resident", file=sys.stderr, flush=True)
+        ms4, per4, _ = time_stack(st4, max(2, args.steps // 2), 1, torch)
+        v4, k4, f4 = summarise(st4, ms4, per4)
+        res["t65536"] = {"workload": wl4.name + " (one layer, alpha of layer 0)",
+                         "value": round(v4, 1), "ms_per_step": round(ms4, 4),
+                         "hbm_frac": f4, "kernels": k4}
+        del st4
         torch.cuda.empty_cache()
 
     if not args.skip_decode:
