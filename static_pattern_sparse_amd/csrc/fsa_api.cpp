@@ -91,7 +91,7 @@ int gcd(int a, int b) {
 void build_taps(int pattern, float alpha, int window, Taps* t) {
   int nb = 0;
   const int* f = base_list(pattern, &nb);
-  t->n = 0;
+  *t = Taps{};                                        // unused slots zero
   for (int k = 0; k < nb; ++k) {
     const double d = static_cast<double>(alpha) * f[k];
     if (d < static_cast<double>(window)) continue;   // inside the window
