@@ -52,7 +52,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 constexpr int kTileQ = 15;          // queries per wavefront tile
 constexpr int kTileK = 14;          // key rows per dk/dv tile
 constexpr int kMaxWinBlocks = 3;    // window blocks: W <= 33
-constexpr int kLdsRowBytes = 72;    // one d-row of V^T: 32 keys (64 B) + pad
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -917,7 +916,7 @@ __device__ __forceinline__ TapSel key_tap_sel(int n, int g) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1))) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
