@@ -31,8 +31,9 @@ counted). The JSON line also carries:
   t65536        one layer (forward and backward) at B=1, H=16, T=65536, D=128;
   decode        a decoding step (one new query per (b, h) in each of the 16
                 layers, B=8, H=8, caches of 4096 rows, W=12): time per step,
-                tokens per second and the mean launch time. Four distinct layer
-                caches serve the 16 layers in turn.
+                tokens per second and the mean launch time, and the step time
+                with its 16 launches captured once in a HIP graph and replayed.
+                Four distinct layer caches serve the 16 layers in turn.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -194,6 +195,29 @@ class DecodeStack:
                     if keep[n] and c[n] <= i))
 
     step = Stack.step
+
+    def graph_ms(self, torch, reps):
+        """Step time with the step's launches captured once in a HIP graph
+        (torch.cuda.CUDAGraph) and replayed: the launches are re-marshalled
+        onto the capture stream."""
+        import ctypes
+        s = torch.cuda.Stream()
+        calls = [(fn, args[:-1] + (ctypes.c_void_p(s.cuda_stream),))
+                 for _, fn, args in self.order]
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            for fn, a in calls:
+                if fn(*a) != 0:
+                    raise RuntimeError("launch failed during capture")
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
 
     def bytes_per_step(self):
         """Algorithmic bytes of one step: every row read once (K and V), the
@@ -483,11 +507,13 @@ def main():
         ms3, per3, _ = time_stack(st3, max(20, args.steps * 5), max(5, args.warmup), torch)
         launch_us = per3["decode"] * 1e3
         nbytes = st3.bytes_per_step() / wl3.layers
+        graph_ms = st3.graph_ms(torch, max(20, args.steps * 5))
         res["decode"] = {
             "workload": wl3.name, "layers": wl3.layers,
             "positions": [int(p) for p in st3.positions],
             "us_per_step": round(ms3 * 1e3, 2),
             "tokens_per_s": round(wl3.B / (ms3 * 1e-3), 1),
+            "graph_us_per_step": round(graph_ms * 1e3, 2),
             "mean_launch_us": round(launch_us, 3),
             "algorithmic_bytes_per_launch": int(nbytes),
             "gbs": round(nbytes / (launch_us * 1e-6) / 1e9, 1),
