@@ -53,7 +53,7 @@ extern "C" {
 /* status codes */
 #define FSA_OK 0
 #define FSA_ERR_INVALID_ARG 1 /* null/misaligned pointer, bad size, bad alpha */
-#define FSA_ERR_UNSUPPORTED 2 /* head dim or dtype this build has no kernel for */
+#define FSA_ERR_UNSUPPORTED 2 /* head dim, dtype or size with no kernel */
 #define FSA_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
 #define FSA_ERR_HIP 4         /* a HIP launch failed; see fsa_last_hip_error() */
 
