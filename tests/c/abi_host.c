@@ -56,6 +56,30 @@ int main(void) {
   CHECK(fsa_forward(NULL, NULL, NULL, FSA_DTYPE_BF16, 1, 1, 16, 96, 1.0f, 4,
                     NULL, NULL, NULL) == FSA_ERR_UNSUPPORTED);
   CHECK(fsa_backward_workspace_size(8, 8, 1024, 64, FSA_DTYPE_BF16) % 256 == 0);
+
+  /* sweep the host planner (under a sanitizer build this checks its memory
+   * use): every pattern bit combination, alphas across the range, windows */
+  for (int pattern = -1; pattern < 9; ++pattern) {
+    for (int ai = 0; ai <= 40; ++ai) {
+      const float alpha = 0.5f + ai / 40.0f;
+      for (int w = 0; w < 45; w += 4) {
+        const int st = fsa_offsets_ex(pattern, alpha, w, dist, t, keep);
+        const int valid = (pattern == 0 || pattern == 1 || pattern == 2 || pattern == 3 ||
+                           pattern == 4 || pattern == 5 || pattern == 6 || pattern == 7) && w >= 1;
+        CHECK(st == (valid ? FSA_OK : FSA_ERR_INVALID_ARG));
+        if (st == FSA_OK)
+          for (int k = 1; k < FSA_NUM_TAPS; ++k) CHECK(dist[k] >= dist[k - 1]);
+      }
+    }
+  }
+  float sched[64];
+  for (int L = 1; L <= 64; ++L)
+    for (int stride = 1; stride < 12; ++stride) {
+      const int st = fsa_schedule(FSA_SCHEDULE_COPRIME, L, 0.5f, 1.5f, stride, sched);
+      int a = stride, b = L;
+      while (b) { const int r = a % b; a = b; b = r; }
+      CHECK(st == (a == 1 ? FSA_OK : FSA_ERR_INVALID_ARG));
+    }
   printf("%s\n", fails ? "failed" : "ok");
   return fails ? 1 : 0;
 }
