@@ -27,7 +27,8 @@ counted). The JSON line also carries:
                 peak; traffic from committed rocprofv3 counter summaries when
                 they match the current kernel source, else null;
   cpu_baseline  the fp64 oracle on the host cores over the same step;
-  t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12;
+  t4096         the same step at B=4, H=8, T=4096, coprime schedule, W=12, and
+                the forward over the window sweep W = 6, 8, 10, 12;
   t65536        one layer (forward and backward) at B=1, H=16, T=65536, D=128;
   decode        a decoding step (one new query per (b, h) in each of the 16
                 layers, B=8, H=8, caches of 4096 rows, W=12): time per step,
@@ -485,6 +486,27 @@ def main():
         v2, k2, f2 = summarise(st2, ms2, per2)
         res["t4096"] = {"workload": wl2.name + " (W=12)", "value": round(v2, 1),
                         "ms_per_step": round(ms2, 4), "hbm_frac": f2, "kernels": k2}
+        # the window sweep of the same stack: forward launches only (the
+        # inputs do not depend on W), host clock over back-to-back launches
+        sweep = {}
+        for W in (6, 8, 10, 12):
+            st2.W = W
+            st2._prepare_calls(torch, F)
+            fwd = [(fn, a) for name, fn, a in st2.order if name == "fwd"]
+            for fn, a in fwd:
+                fn(*a)
+            torch.cuda.synchronize()
+            reps = max(2, args.steps // 2)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                for fn, a in fwd:
+                    fn(*a)
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / (reps * len(fwd))
+            ab = algo_bytes(wl2.D, 2, st2.out_bytes)["fwd"] * wl2.B * wl2.H * wl2.T
+            sweep[f"W{W}"] = {"fwd_us": round(us, 2),
+                              "hbm_frac": round(ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        res["t4096"]["window_sweep_forward"] = sweep
         del st2
         torch.cuda.empty_cache()
 
