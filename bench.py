@@ -22,6 +22,7 @@ slows the launch that follows.
 
 value = layers * B * H * T / step time (token-heads per second, every layer
 counted). The JSON line also carries:
+  copy_gbs      a plain 1 GiB device copy's read+write GB/s, for context;
   roofline      the dominant kernel's algorithmic bytes per launch divided by
                 its mean event-to-event launch time, against the 8 TB/s HBM
                 peak; traffic from committed rocprofv3 counter summaries when
@@ -346,6 +347,27 @@ def load_traffic(kernel, per_launch_tokens):
     return float(b.group(1)) * per_launch_tokens
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Achievable HBM bandwidth on this device for context: a plain 1 GiB
+    device-to-device copy (read + write bytes over the mean copy time)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / sec / 1e9, 1)
+
+
 # ------------------------------------------------------------- CPU baseline
 def _oracle_layer(args):
     import numpy as np
@@ -472,6 +494,8 @@ def main():
                    "pass": "forward+backward"},
         "roofline": roofline,
         "hbm_frac": frac,
+        # context: a plain 1 GiB device copy on the same GPU (read + write)
+        "copy_gbs": copy_bandwidth(torch),
         "kernels": kernels,
         "launches_per_kernel": counts,
     }
