@@ -163,6 +163,33 @@ def _shape(q):
     return tuple(int(s) for s in q.shape)
 
 
+def _need(t, shape, dtype, name):
+    """A caller-supplied device tensor must have exactly the shape and dtype
+    the C ABI assumes for that pointer (the library sees only addresses)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def _rows(q, others):
+    for x in others:
+        if x.shape != q.shape or x.dtype != q.dtype or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError("q, k, v (and dout) must share shape and dtype and be "
+                             "contiguous device tensors")
+
+
+def _workspace(ws, nbytes):
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return ws
+
+
 def _out_buffer(out, out_dtype, shape, device, pattern):
     """The output tensor (fp32 or bf16) and the flags that describe it."""
     import torch
@@ -185,12 +212,11 @@ def fsa_forward(q, k, v, alpha, window, out=None, lse=None, stream=None,
     `out`) and lse [B,H,T] fp32 of one layer."""
     import torch
     B, H, T, D = _shape(q)
-    for x in (k, v):
-        if x.shape != q.shape or x.dtype != q.dtype or not x.is_contiguous():
-            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    _rows(q, (k, v))
     out, flags = _out_buffer(out, out_dtype, (B, H, T, D), q.device, pattern)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    _need(lse, (B, H, T), torch.float32, "lse")
     st = lib().fsa_forward_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H,
                               T, D, float(alpha), int(window), flags,
                               _ptr(out), _ptr(lse), _stream(stream))
@@ -209,19 +235,21 @@ def fsa_backward(q, k, v, dout, lse, alpha, window, dq=None, dk=None, dv=None,
     """dq, dk, dv [B,H,T,D] fp32 and dalpha [1] fp32 of one layer."""
     import torch
     B, H, T, D = _shape(q)
-    for x in (k, v, dout):
-        if x.shape != q.shape or x.dtype != q.dtype or not x.is_contiguous():
-            raise ValueError("q, k, v, dout must share shape, dtype and be contiguous")
+    _rows(q, (k, v, dout))
     dt = _dtype_code(q)
-    mk = lambda: torch.empty((B, H, T, D), dtype=torch.float32, device=q.device)
-    dq = mk() if dq is None else dq
-    dk = mk() if dk is None else dk
-    dv = mk() if dv is None else dv
+    f32 = torch.float32
+    mk = lambda: torch.empty((B, H, T, D), dtype=f32, device=q.device)
+    dq = mk() if dq is None else _need(dq, (B, H, T, D), f32, "dq")
+    dk = mk() if dk is None else _need(dk, (B, H, T, D), f32, "dk")
+    dv = mk() if dv is None else _need(dv, (B, H, T, D), f32, "dv")
+    _need(lse, (B, H, T), f32, "lse")
     if dalpha is None:
-        dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
+        dalpha = torch.empty(1, dtype=f32, device=q.device)
+    _need(dalpha, (1,), f32, "dalpha")
     nbytes = fsa_backward_workspace_size(B, H, T, D, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, nbytes)
     st = lib().fsa_backward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                             dt, B, H, T, D, float(alpha), int(window),
                             int(pattern), _ptr(dq),
@@ -240,7 +268,12 @@ def fsa_backward_dq(q, k, v, dout, lse, alpha, window, dq, workspace,
                     stream=None, pattern=FSA_PATTERN_FIB):
     """Stage 1 of the backward pass: dq, plus per-row terms and dalpha
     partials in `workspace`."""
+    import torch
     B, H, T, D = _shape(q)
+    _rows(q, (k, v, dout))
+    _need(lse, (B, H, T), torch.float32, "lse")
+    _need(dq, (B, H, T, D), torch.float32, "dq")
+    _workspace(workspace, fsa_backward_workspace_size(B, H, T, D, _dtype_code(q)))
     st = lib().fsa_backward_dq_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                _ptr(lse), _dtype_code(q), B, H, T, D,
                                float(alpha), int(window), int(pattern),
@@ -253,7 +286,14 @@ def fsa_backward_dkdv(q, k, v, dout, lse, alpha, window, dk, dv, dalpha,
                       workspace, stream=None, pattern=FSA_PATTERN_FIB):
     """Stage 2 of the backward pass: dk, dv, and dalpha[0] from the stage-1
     partials."""
+    import torch
     B, H, T, D = _shape(q)
+    _rows(q, (k, v, dout))
+    _need(lse, (B, H, T), torch.float32, "lse")
+    _need(dk, (B, H, T, D), torch.float32, "dk")
+    _need(dv, (B, H, T, D), torch.float32, "dv")
+    _need(dalpha, (1,), torch.float32, "dalpha")
+    _workspace(workspace, fsa_backward_workspace_size(B, H, T, D, _dtype_code(q)))
     st = lib().fsa_backward_dkdv_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                  _ptr(lse), _dtype_code(q), B, H, T, D,
                                  float(alpha), int(window), int(pattern),
@@ -282,6 +322,7 @@ def fsa_decode(q, k_cache, v_cache, pos, alpha, window, out=None, lse=None,
     out, flags = _out_buffer(out, out_dtype, (B, H, D), q.device, pattern)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need(lse, (B, H), torch.float32, "lse")
     st = lib().fsa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
                           B, H, T_cap, D, _ptr(pos), float(alpha), int(window),
                           flags, _ptr(out), _ptr(lse), _stream(stream))

@@ -208,3 +208,16 @@ def test_decode_validation_codes():
     assert _dec(B=300, H=300) == F.FSA_ERR_UNSUPPORTED
     # no query at all is a no-op
     assert _dec(B=0, q=0, k=0, v=0, pos=0, out=0, lse=0) == F.FSA_OK
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The binding checks every caller-supplied tensor against the shape and
+    dtype the C call assumes for its pointer (CPU tensors are rejected first)."""
+    import torch
+    q = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        F.fsa_forward(q, q, q, 1.0, 4)                     # not device tensors
+    with pytest.raises(ValueError):
+        F._need(torch.zeros(3), (4,), torch.float32, "x")
+    with pytest.raises(ValueError):
+        F._rows(q, (torch.zeros(1, 1, 15, 64),))
