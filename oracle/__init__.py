@@ -7,4 +7,4 @@ from .fsa_oracle import (BASES, FIB, MODES, POW2, SCHEDULE_COPRIME,  # noqa: F40
                          SCHEDULE_FIXED, TapTable,
                          SCHEDULE_LINEAR, backward, backward_slab, decode, dkdv_rows,
                          dq_rows, forward, forward_rows, forward_slab,
-                         offset_table, schedule)
+                         offset_table, rope, schedule)

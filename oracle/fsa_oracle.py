@@ -39,12 +39,17 @@ Readings taken where the page leaves a step open:
 * R8 d(alpha) at an integer d_k uses the right-hand slope K[a+1] - K[a].
 * R9 the schedule for L layers: linear alpha_l = a_min + (a_max-a_min)*l/(L-1)
   evaluated in fp64 and rounded once to fp32; coprime out[(s*l) mod L] = lin[l].
-* R10 the power-of-two control base (Methodology > Control variables) is the
+* R12 RoPE (rope below): the page says only that RoPE is applied before the
+  gather and that it is native, unscaled RoPE [DSFS: Significance and
+  claims]. Reading: rotate-half pairs (m, m + D/2) for m < D/2, frequency
+  theta_m = base^(-2m/D), row t at position pos0 + t, the pair turned by the
+  angle position * theta_m.
+* R14 the power-of-two control base (Methodology > Control variables) is the
   fifteen terms 1, 2, 4, ..., 16384: the page's examples of offsets first met at
   4096 tokens (1024, 2048; Core contributions and results > 3. Length
   extrapolation, base sensitivity) need a ladder past 987, and fifteen terms
   match the Fibonacci list's count.
-* R11 the rounded (mask) mode of the static runs (Core contributions and
+* R15 the rounded (mask) mode of the static runs (Core contributions and
   results > 2. Learned dilation is inert, efficiency) attends row i - round(d_k)
   with round to nearest, ties to even; a term is kept under the same rule
   d_k >= W and applies to query i when i >= round(d_k). The attended rows do
@@ -66,7 +71,7 @@ import numpy as np
 # Fibonacci distances, 1 through 987, the leading 1 taken once.
 FIB = (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987)
 
-# [DSFS: Methodology > Control variables] -- the power-of-two base, reading R10.
+# [DSFS: Methodology > Control variables] -- the power-of-two base, reading R14.
 POW2 = tuple(2 ** n for n in range(15))
 
 BASES = {"fib": FIB, "pow2": POW2}
@@ -134,7 +139,7 @@ def offset_table(alpha: float, window: int, round_alpha_to_fp32: bool = True,
       lerp:  c_k = ceil(d_k) (distance to the lower interpolation row),
              t_k = c_k - d_k in [0, 1) (weight of the upper row, reading R4),
              slope_k = -f_k (the sample position i - alpha*f_k moves with alpha);
-      round: c_k = round(d_k), ties to even, t_k = 0, slope_k = 0 (reading R11).
+      round: c_k = round(d_k), ties to even, t_k = 0, slope_k = 0 (reading R15).
 
     `round_alpha_to_fp32=False` keeps alpha in fp64; only finite-difference
     tests use it, to step alpha by less than an fp32 ulp.
@@ -250,7 +255,7 @@ def backward_slab(q, k, v, dout, alpha, window, table=None, base="fib",
       dalpha = sum over taps and queries of slope_k * [ scale*dS * q_i.(K[a+1]-K[a])
                                                         + p * dout_i.(V[a+1]-V[a]) ]
     with slope_k = -f_k when the distance interpolates and 0 in the rounded
-    mode (reading R11)
+    mode (reading R15)
     [DSFS: Methodology > Architecture and attention > Implementation (gradient
     to alpha); Experimental variables > Learned]. Reading R8 fixes the slope at
     integer distances.
@@ -500,3 +505,34 @@ def decode(q, k_cache, v_cache, pos, alpha, window, base="fib", mode="lerp"):
             p = np.exp(s - lse[b, h])
             out[b, h] = (p[:, None] * np.array(values)).sum(axis=0)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# rope: the rotation applied to queries and keys before the gather
+# ---------------------------------------------------------------------------
+def rope(x, base, pos0=None, inverse=False):
+    """Rotary position embedding of rows x [B, H, T, D] in fp64 (reading R12):
+    RoPE is applied to queries and keys before the gather [DSFS: Methodology >
+    Architecture and attention > Implementation], native and unscaled [DSFS:
+    Significance and claims]. Row t of batch entry b stands at position
+    pos0[b] + t (pos0 None: t). For each m < D/2 the pair (x[m], x[m + D/2])
+    turns by the angle position * base**(-2m/D); inverse=True turns by the
+    negated angle, the transpose of the rotation (what maps a gradient with
+    respect to rotated rows back to the rows before rotation)."""
+    x = np.asarray(x, dtype=np.float64)
+    B, H, T, D = x.shape
+    if D % 2:
+        raise ValueError("RoPE pairs need an even D")
+    half = D // 2
+    theta = np.array([float(base) ** (-2.0 * m / D) for m in range(half)])
+    start = np.zeros(B, dtype=np.int64) if pos0 is None else np.asarray(pos0, dtype=np.int64)
+    sign = -1.0 if inverse else 1.0
+    y = np.empty_like(x)
+    for b in range(B):
+        position = (start[b] + np.arange(T)).astype(np.float64)
+        angle = position[:, None] * theta[None, :]          # [T, D/2]
+        c, s = np.cos(angle), sign * np.sin(angle)
+        lo, hi = x[b, :, :, :half], x[b, :, :, half:]
+        y[b, :, :, :half] = lo * c - hi * s
+        y[b, :, :, half:] = lo * s + hi * c
+    return y
