@@ -35,7 +35,14 @@ counted). The JSON line also carries:
                 layers, B=8, H=8, caches of 4096 rows, W=12): time per step,
                 tokens per second and the mean launch time, and the step time
                 with its 16 launches captured once in a HIP graph and replayed.
-                Four distinct layer caches serve the 16 layers in turn.
+                Four distinct layer caches serve the 16 layers in turn;
+  rope          the RoPE pass at the training size (B=8, H=8, T=1024, D=64,
+                base 10000; q and k of every layer) and at B=1, H=16,
+                T=65536, D=128 (base 500000): pre-RoPE rows into bf16 rows,
+                and fp32 gradients turned back; mean launch time and GB/s
+                over the algorithmic bytes (each element read and written
+                once). Not part of the step: the attention step takes
+                post-RoPE inputs.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -229,6 +236,50 @@ class DecodeStack:
         per_query = wl.D * in_b + 4 * wl.D + 4
         return (self.rows_per_step * 2 * wl.D * in_b
                 + wl.layers * wl.B * wl.H * per_query)
+
+
+class RopeStack:
+    """Device buffers of the RoPE pass over one workload's shape: per layer the
+    pre-RoPE q and k (bf16, rotated into bf16 rows, "rope") and the fp32
+    gradients dq and dk (turned back, "rope_inv"). `sets` distinct buffer
+    sets (more than the Infinity Cache in all) serve the layers in turn."""
+
+    def __init__(self, wl, torch, F, I, layers, sets):
+        import ctypes
+        self.wl, self.layers = wl, layers
+        B, H, T, D = wl.B, wl.H, wl.T, wl.D
+        self.sets = []
+        # seeded N(0, 1) rows drawn on the device (the 65536-token size is too
+        # large to draw on the host at bench start)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(I.SEED_ROOT + wl.workload_id)
+        for c in range(sets):
+            draw = lambda dt: torch.randn((B, H, T, D), generator=gen, device="cuda").to(dt)
+            t = {"q": draw(torch.bfloat16), "k": draw(torch.bfloat16),
+                 "dq": draw(torch.float32), "dk": draw(torch.float32)}
+            for n in ("q", "k"):
+                t[n + "r"] = torch.empty_like(t[n])
+            for n in ("dq", "dk"):
+                t[n + "p"] = torch.empty_like(t[n])
+            self.sets.append(t)
+        lib = F.lib()
+        vp, f32 = ctypes.c_void_p, ctypes.c_float
+        stream = vp(torch.cuda.current_stream().cuda_stream)
+        base = f32(wl.rope_base)
+        bf, fp = F.FSA_DTYPE_BF16, F.FSA_DTYPE_F32
+        self.order = []
+        for l in range(layers):
+            p = {n: vp(x.data_ptr()) for n, x in self.sets[l % sets].items()}
+            for n in ("q", "k"):
+                self.order.append(("rope", lib.fsa_rope, (p[n], bf, B, H, T, D, base, None,
+                                                          0, p[n + "r"], bf, stream)))
+        for l in reversed(range(layers)):
+            p = {n: vp(x.data_ptr()) for n, x in self.sets[l % sets].items()}
+            for n in ("dq", "dk"):
+                self.order.append(("rope_inv", lib.fsa_rope, (p[n], fp, B, H, T, D, base,
+                                                              None, 1, p[n + "p"], fp, stream)))
+
+    step = Stack.step
 
 
 class Events:
@@ -430,6 +481,7 @@ def main():
     ap.add_argument("--skip-t4096", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-t65536", action="store_true")
+    ap.add_argument("--skip-rope", action="store_true")
     ap.add_argument("--out-bf16", action="store_true",
                     help="the forward writes out in bf16 (FSA_OUT_BF16)")
     ap.add_argument("--pattern", default="fib",
@@ -566,6 +618,26 @@ def main():
             "bound": "latency"}
         del st3
         torch.cuda.empty_cache()
+
+    if not args.skip_rope:
+        res["rope"] = {}
+        wl5 = I.WORKLOADS["linear16_bf16_b1h16t65536d128_w12"]
+        for key, w, layers, sets in (("t1024", wl, wl.layers, 4), ("t65536", wl5, 2, 2)):
+            st5 = RopeStack(w, torch, F, I, layers, sets)
+            print(f"[bench] rope pass {key} resident", file=sys.stderr, flush=True)
+            ms5, per5, _ = time_stack(st5, max(4, args.steps), max(2, args.warmup), torch)
+            elems = w.B * w.H * w.T * w.D
+            rope = {"workload": f"rope_b{w.B}h{w.H}t{w.T}d{w.D}_base{int(w.rope_base)}",
+                    "launches_per_step": len(st5.order), "ms_per_step": round(ms5, 4)}
+            for name, nbytes in (("rope", elems * (2 + 2)), ("rope_inv", elems * (4 + 4))):
+                us = per5[name] * 1e3
+                gbs = nbytes / (us * 1e-6) / 1e9
+                rope[name] = {"mean_launch_us": round(us, 3),
+                              "algorithmic_bytes_per_launch": nbytes,
+                              "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            res["rope"][key] = rope
+            del st5
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

@@ -262,6 +262,43 @@ int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
                float alpha, int window, int pattern, void* out, float* lse,
                void* stream);
 
+/*
+ * fsa_rope -- rotary position embedding of query or key rows, the pass that
+ * precedes the gather (the attention entry points take its output).
+ * [DSFS: Methodology > Architecture and attention > Implementation (RoPE is
+ * applied before the gather); Significance and claims (native RoPE, no
+ * scaling); Core contributions and results > 3. Length extrapolation,
+ * mechanism (a fixed offset keeps the same rotation angle at every position)]
+ * The pages fix neither pairing nor frequencies; this library uses the
+ * rotate-half pairing: for m < D/2 the pair (x[m], x[m + D/2]) of row t of
+ * slab (b, h) turns by the angle p * base^(-2m/D) at position
+ * p = pos0[b] + t:
+ *   y[m]       = x[m] cos - x[m + D/2] sin,
+ *   y[m + D/2] = x[m] sin + x[m + D/2] cos.
+ *   x         device [B][H][T][D] of in_dtype (FSA_DTYPE_F32 or _BF16),
+ *             16-byte aligned, read.
+ *   y         device [B][H][T][D] of out_dtype, 16-byte aligned, written
+ *             (bf16: round to nearest even from the fp32 result). y == x
+ *             rotates in place when in_dtype == out_dtype; other overlaps
+ *             are not allowed.
+ *   pos0      device int32[B], 4-byte aligned: position of row 0 per batch
+ *             entry (a decoding step passes T = 1 and its positions), or
+ *             NULL for position t.
+ *   base      frequency base (10000, 500000, ...), finite and > 1.
+ *   inverse   nonzero: turn by the negated angles, the transpose of the
+ *             rotation; applied to the gradient with respect to rotated rows
+ *             (fsa_backward's dq, dk) it gives the gradient with respect to
+ *             the rows before rotation.
+ * Angles are reduced modulo 2 pi in fp64 and rotated in fp32. Returns
+ * FSA_ERR_INVALID_ARG for a null or misaligned pointer, negative sizes, an odd
+ * D or a bad base, or x == y with two dtypes; FSA_ERR_UNSUPPORTED for another
+ * dtype, D not a multiple of 8 or above 1024, or a grid beyond 2^31
+ * workgroups. B*H*T == 0 is a no-op.
+ */
+int fsa_rope(const void* x, int in_dtype, int B, int H, int T, int D,
+             float base, const int32_t* pos0, int inverse, void* y,
+             int out_dtype, void* stream);
+
 /* fsa_status_string -- static text for a status code. */
 const char* fsa_status_string(int status);
 

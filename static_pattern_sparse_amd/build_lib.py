@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfsa.so")
-SOURCES = ["fsa_api.cpp", "fsa_vec.hip", "fsa_mfma.hip", "fsa_decode.hip"]
+SOURCES = ["fsa_api.cpp", "fsa_vec.hip", "fsa_mfma.hip", "fsa_decode.hip", "fsa_rope.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

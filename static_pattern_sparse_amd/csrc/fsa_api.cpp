@@ -432,6 +432,30 @@ int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
                                   static_cast<hipStream_t>(stream)));
 }
 
+int fsa_rope(const void* x, int in_dtype, int B, int H, int T, int D,
+             float base, const int32_t* pos0, int inverse, void* y,
+             int out_dtype, void* stream) {
+  if (B < 0 || H < 0 || T < 0 || D < 2 || (D & 1) != 0 || !std::isfinite(base) ||
+      !(base > 1.f))
+    return FSA_ERR_INVALID_ARG;
+  if ((in_dtype != FSA_DTYPE_F32 && in_dtype != FSA_DTYPE_BF16) ||
+      (out_dtype != FSA_DTYPE_F32 && out_dtype != FSA_DTYPE_BF16))
+    return FSA_ERR_UNSUPPORTED;
+  // one thread per 4 pairs of a row; the grid is one-dimensional
+  if ((D & 7) != 0 || D > 1024) return FSA_ERR_UNSUPPORTED;
+  if (rope_blocks(B, H, T, D) > 0x7fffffffLL) return FSA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(B) * H * T == 0) return FSA_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y) ||
+      (pos0 != nullptr && (reinterpret_cast<uintptr_t>(pos0) & 3u) != 0))
+    return FSA_ERR_INVALID_ARG;
+  // in place only with one element size: rows of different widths would
+  // overlap other threads' rows
+  if (x == y && in_dtype != out_dtype) return FSA_ERR_INVALID_ARG;
+  return hip_status(launch_rope(x, in_dtype, B, H, T, D, static_cast<double>(base),
+                                pos0, inverse != 0, y, out_dtype,
+                                static_cast<hipStream_t>(stream)));
+}
+
 const char* fsa_status_string(int status) {
   switch (status) {
     case FSA_OK: return "ok";

@@ -65,6 +65,15 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype,
                          const Taps& taps, void* out, bool out_bf16, float* lse,
                          hipStream_t s);
 
+// rotary position embedding pass (fsa_rope.hip): rows [B][H][T][D] of
+// in_dtype -> out_dtype, row t of batch entry b at position pos0[b] + t
+// (pos0 may be null: position t); inverse turns by the negated angles
+hipError_t launch_rope(const void* x, int in_dtype, int B, int H, int T, int D,
+                       double base, const int* pos0, bool inverse, void* y,
+                       int out_dtype, hipStream_t s);
+// workgroups the pass launches (the 1-D grid must stay below 2^31)
+long long rope_blocks(int B, int H, int T, int D);
+
 // lane-per-row kernels (fsa_vec.hip)
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,

@@ -45,7 +45,7 @@ EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_offsets_ex", "fsa_forward",
            "fsa_forward_ex", "fsa_backward_workspace_size", "fsa_backward",
            "fsa_backward_ex", "fsa_backward_dq", "fsa_backward_dq_ex",
            "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_decode",
-           "fsa_status_string", "fsa_last_hip_error")
+           "fsa_rope", "fsa_status_string", "fsa_last_hip_error")
 
 _lib = None
 
@@ -101,6 +101,8 @@ def lib():
     L.fsa_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, i32,
                              i32, vp, vp, vp]
     L.fsa_decode.restype = i32
+    L.fsa_rope.argtypes = [vp, i32, i32, i32, i32, i32, f32, vp, i32, vp, i32, vp]
+    L.fsa_rope.restype = i32
     L.fsa_status_string.argtypes = [i32]
     L.fsa_status_string.restype = ctypes.c_char_p
     L.fsa_last_hip_error.argtypes = []
@@ -328,3 +330,26 @@ def fsa_decode(q, k_cache, v_cache, pos, alpha, window, out=None, lse=None,
                           flags, _ptr(out), _ptr(lse), _stream(stream))
     _check("fsa_decode", st)
     return out, lse
+
+
+def fsa_rope(x, base, pos0=None, inverse=False, out=None, out_dtype=None,
+             stream=None):
+    """Rotary position embedding of rows x [B,H,T,D] (fp32 or bf16): row t of
+    batch entry b at position pos0[b] + t (pos0: int32 [B] on the device, or
+    None for t). inverse=True turns by the negated angles. Returns `out`
+    (default: a new tensor of out_dtype, else x's dtype); out may be x itself
+    when the dtypes agree."""
+    import torch
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, T, D] device tensor")
+    B, H, T, D = (int(s) for s in x.shape)
+    if out is None:
+        out = torch.empty_like(x, dtype=x.dtype if out_dtype is None else out_dtype)
+    _need(out, (B, H, T, D), out.dtype, "out")
+    if pos0 is not None:
+        _need(pos0, (B,), torch.int32, "pos0")
+    st = lib().fsa_rope(_ptr(x), _dtype_code(x), B, H, T, D, float(base),
+                        _ptr(pos0), int(bool(inverse)), _ptr(out),
+                        _dtype_code(out), _stream(stream))
+    _check("fsa_rope", st)
+    return out

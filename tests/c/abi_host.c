@@ -56,6 +56,12 @@ int main(void) {
   CHECK(fsa_forward(NULL, NULL, NULL, FSA_DTYPE_BF16, 1, 1, 16, 96, 1.0f, 4,
                     NULL, NULL, NULL) == FSA_ERR_UNSUPPORTED);
   CHECK(fsa_backward_workspace_size(8, 8, 1024, 64, FSA_DTYPE_BF16) % 256 == 0);
+  CHECK(fsa_rope(NULL, FSA_DTYPE_BF16, 1, 1, 16, 64, 10000.0f, NULL, 0, NULL,
+                 FSA_DTYPE_BF16, NULL) == FSA_ERR_INVALID_ARG);
+  CHECK(fsa_rope(NULL, FSA_DTYPE_BF16, 1, 1, 16, 60, 10000.0f, NULL, 0, NULL,
+                 FSA_DTYPE_BF16, NULL) == FSA_ERR_UNSUPPORTED);
+  CHECK(fsa_rope(NULL, FSA_DTYPE_F32, 1, 1, 0, 64, 10000.0f, NULL, 1, NULL,
+                 FSA_DTYPE_F32, NULL) == FSA_OK);
 
   /* sweep the host planner (under a sanitizer build this checks its memory
    * use): every pattern bit combination, alphas across the range, windows */

@@ -221,3 +221,43 @@ def test_binding_rejects_mismatched_buffers():
         F._need(torch.zeros(3), (4,), torch.float32, "x")
     with pytest.raises(ValueError):
         F._rows(q, (torch.zeros(1, 1, 15, 64),))
+
+
+def _rope(**kw):
+    a = dict(x=FAKE, din=1, B=2, H=3, T=64, D=64, base=10000.0, pos0=0,
+             inverse=0, y=FAKE + 4096, dout=1)
+    a.update(kw)
+    ptr = ("x", "pos0", "y")
+    order = ("x", "din", "B", "H", "T", "D", "base", "pos0", "inverse", "y", "dout")
+    return F.lib().fsa_rope(*(ctypes.c_void_p(a[n]) if n in ptr else a[n]
+                              for n in order), None)
+
+
+def test_rope_validation_codes():
+    """Argument checks of fsa_rope run before any HIP call (no launch here:
+    every call below is rejected, or is the empty no-op)."""
+    assert _rope(x=0) == F.FSA_ERR_INVALID_ARG
+    assert _rope(y=0) == F.FSA_ERR_INVALID_ARG
+    assert _rope(x=FAKE + 8) == F.FSA_ERR_INVALID_ARG       # misaligned rows
+    assert _rope(pos0=FAKE + 2) == F.FSA_ERR_INVALID_ARG    # misaligned int32
+    assert _rope(D=63) == F.FSA_ERR_INVALID_ARG             # pairs need an even D
+    assert _rope(D=0) == F.FSA_ERR_INVALID_ARG
+    assert _rope(B=-1) == F.FSA_ERR_INVALID_ARG
+    assert _rope(base=1.0) == F.FSA_ERR_INVALID_ARG
+    assert _rope(base=float("nan")) == F.FSA_ERR_INVALID_ARG
+    assert _rope(base=float("inf")) == F.FSA_ERR_INVALID_ARG
+    assert _rope(y=FAKE, din=0, dout=1) == F.FSA_ERR_INVALID_ARG   # in place, two widths
+    assert _rope(D=60) == F.FSA_ERR_UNSUPPORTED            # not a multiple of 8
+    assert _rope(D=2048) == F.FSA_ERR_UNSUPPORTED
+    assert _rope(din=7) == F.FSA_ERR_UNSUPPORTED
+    assert _rope(dout=2) == F.FSA_ERR_UNSUPPORTED
+    assert _rope(B=65535, H=65535, T=65535) == F.FSA_ERR_UNSUPPORTED   # grid limit
+    # no row at all is a no-op
+    assert _rope(T=0, x=0, y=0) == F.FSA_OK
+
+
+def test_rope_binding_checks_buffers():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        F.fsa_rope(x, 10000.0)                              # not a device tensor

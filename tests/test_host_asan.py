@@ -14,6 +14,8 @@ import subprocess
 
 import pytest
 
+from static_pattern_sparse_amd import build_lib
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "static_pattern_sparse_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -32,7 +34,8 @@ def test_host_code_under_sanitizers(tmp_path):
         [HIPCC, "-c", "-fPIC", "-O1", "-g", "-std=c++17",
          "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
          *INC, "-o", os.path.join(d, "api.o"), os.path.join(CSRC, "fsa_api.cpp")])]
-    for name in ("fsa_vec", "fsa_decode", "fsa_mfma"):
+    kernels = [os.path.splitext(n)[0] for n in build_lib.SOURCES if n.endswith(".hip")]
+    for name in kernels:
         jobs.append(subprocess.Popen(
             [HIPCC, "-c", *KERNEL_FLAGS, *INC, "-o", os.path.join(d, name + ".o"),
              os.path.join(CSRC, name + ".hip")],
@@ -40,7 +43,7 @@ def test_host_code_under_sanitizers(tmp_path):
     assert all(j.wait(timeout=600) == 0 for j in jobs)
     lib = os.path.join(d, "libfsa.so")
     subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", lib,
-                    *(os.path.join(d, n + ".o") for n in ("api", "fsa_vec", "fsa_decode", "fsa_mfma"))],
+                    *(os.path.join(d, n + ".o") for n in ["api", *kernels])],
                    check=True)
     exe = os.path.join(d, "abi_host")
     subprocess.run([CLANG, "-std=c99", "-g", "-fsanitize=address,undefined",
