@@ -1003,6 +1003,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 
   for (int p = 0; p < nwp; ++p) {
     if (p > 0)
       stage_two<D>(sq, sg, tl, rowb + 32 * p, 2 * p + 1 < nqb ? rowb + 32 * p + 16 : INT_MIN, lds);
+    // {L2, Delta} of queries ib+4g .. ib+4g+3 of both blocks, one 8-byte load
+    // each, issued with the stage so that one wait covers both (the buffer
+    // range check rejects a whole access that crosses the slab edge, so a
+    // wider load would lose a valid query next to row -1 or T)
+    uint2 qld[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qld[hf][j] = bld8(rd, (rowb + 16 * (2 * p + hf) + 4 * g + j) * 8);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     float pv[8], dsv[8];
@@ -1015,15 +1025,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 
       nat_operand<D>(lds + (2 + hf) * Tl::kBlockBytes, tl, ga);
       const f32x4 s = mfma_rows<D>(qa, kb);
       const f32x4 d = mfma_rows<D>(ga, vb);
-      // {L2, Delta} of queries ib+4g .. ib+4g+3, one 8-byte load each: the
-      // buffer range check rejects a whole access that crosses the slab
-      // edge, so a wider load would lose a valid query next to row -1 or T.
       float qL[4], qD[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint2 x = bld8(rd, (ib + 4 * g + j) * 8);
-        qL[j] = __uint_as_float(x.x);
-        qD[j] = __uint_as_float(x.y);
+        qL[j] = __uint_as_float(qld[hf][j].x);
+        qD[j] = __uint_as_float(qld[hf][j].y);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
