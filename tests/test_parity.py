@@ -214,6 +214,35 @@ def test_integer_offsets_are_pure_gather():
     check_forward(x, "bf16", 1.0, 1000)
 
 
+@pytest.mark.parametrize("dtype,qscale,alpha,W", [("bf16", 8.0, 0.7317, 12),
+                                                  ("bf16", 32.0, 1.2913, 6),
+                                                  ("f32", 8.0, 0.8333333, 12)])
+def test_sharp_scores(dtype, qscale, alpha, W):
+    """q scaled by a power of two (exact in both dtypes): scores of tens of
+    units, so the softmax is dominated by a few entries and the running max
+    moves often and far (the lazy rescale of the tile kernels and the online
+    max of the lane-per-row kernels)."""
+    _say("sharp scores", dtype, qscale, alpha, W)
+    alpha = float(np.float32(alpha))
+    x = _rand_inputs(2, 2, 900, 64, dtype, 40 + int(qscale))
+    x["q"] = x["q"] * np.float32(qscale)
+    out, lse = gpu_forward(x, dtype, alpha, W)
+    dq, dk, dv, da = gpu_backward(x, dtype, alpha, W, lse)
+    xd = _f64(x)
+    ro, rl = O.forward(xd["q"], xd["k"], xd["v"], alpha, W)
+    rq, rk, rv, ra = O.backward(xd["q"], xd["k"], xd["v"], xd["dout"], alpha, W)
+    # dk grows with |q| (up to about 80 at q x 32): the max-abs bars, set for
+    # outputs of order 1-4, are applied relative to a quarter of each output's
+    # largest magnitude when that exceeds 1
+    for name, g, r in (("out", out, ro), ("lse", lse, rl), ("dq", dq, rq),
+                       ("dk", dk, rk), ("dv", dv, rv)):
+        tol = TOL[dtype] * max(1.0, float(np.abs(r).max()) / 4.0)
+        e = _maxerr(_np(g), r)
+        assert e <= tol, f"{name} err {e} > {tol}"
+    a = float(da.item())
+    assert abs(a - ra) <= DALPHA_RTOL * abs(ra), f"dalpha {a} vs {ra}"
+
+
 def test_empty_problem_is_noop():
     torch = _torch()
     from static_pattern_sparse_amd import fsa as F
