@@ -2,7 +2,8 @@
 
 The entry points allocate nothing, never synchronise and launch only on the
 stream they are given, so a caller can capture them. The graph here holds a
-forward, the two backward stages and a decoding step; it is replayed several
+forward, the two backward stages, a decoding step and RoPE passes (forward and
+inverse, with device start positions); it is replayed several
 times, with eager work and synchronisations in between, and every replay must
 reproduce the eager results bit for bit.
 """
@@ -35,7 +36,8 @@ def test_captured_calls_replay_exactly():
     def bufs():
         f = lambda *s: torch.full(s, float("nan"), device="cuda")
         return dict(out=f(B, H, T, D), lse=f(B, H, T), dq=f(B, H, T, D), dk=f(B, H, T, D),
-                    dv=f(B, H, T, D), da=f(1), dout=f(B, H, D), dlse=f(B, H))
+                    dv=f(B, H, T, D), da=f(1), dout=f(B, H, D), dlse=f(B, H),
+                    qr=f(B, H, T, D).to(torch.bfloat16), dqp=f(B, H, T, D))
 
     ws = torch.empty(F.fsa_backward_workspace_size(B, H, T, D, F.FSA_DTYPE_BF16),
                      dtype=torch.uint8, device="cuda")
@@ -46,6 +48,8 @@ def test_captured_calls_replay_exactly():
         F.fsa_backward_dkdv(q, k, v, g, o["lse"], alpha, W, o["dk"], o["dv"], o["da"], ws,
                             stream=stream)
         F.fsa_decode(dq_, dk_, dv_, pos, alpha, W, out=o["dout"], lse=o["dlse"], stream=stream)
+        F.fsa_rope(q, 10000.0, pos, out=o["qr"], stream=stream)
+        F.fsa_rope(o["dq"], 10000.0, pos, inverse=True, out=o["dqp"], stream=stream)
 
     ref = bufs()
     run(ref, None)
