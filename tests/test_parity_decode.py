@@ -158,3 +158,26 @@ def test_decode_bf16_out():
     torch.cuda.synchronize()
     assert ob.dtype == torch.bfloat16
     assert torch.equal(ob, o32.to(torch.bfloat16)) and torch.equal(lb, l32)
+
+
+def _draw_decode(seed):
+    r = np.random.default_rng(90000 + seed)
+    B, H = int(r.integers(1, 6)), int(r.integers(1, 4))
+    T = int(r.integers(1, 3000))
+    D = int(r.choice([64, 128]))
+    dtype = "f32" if r.random() < 0.3 else "bf16"
+    alpha = float(np.float32(r.uniform(0.5, 1.5)))
+    W = int(r.integers(1, 80))
+    pattern = str(r.choice(sorted(ORACLE_PATTERN)))
+    pos = [int(p) for p in r.integers(0, T, B)]
+    return B, H, T, D, dtype, alpha, W, pattern, pos
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random(seed):
+    """Seeded random batch sizes, cache lengths, head dims, dtypes, windows,
+    patterns and positions."""
+    B, H, T, D, dtype, alpha, W, pattern, pos = _draw_decode(seed)
+    _say("decode random", seed, B, H, T, D, dtype, alpha, W, pattern, pos)
+    x = I.make_decode_inputs(B, H, T, D, dtype, 300 + seed % 7, 0, pos)
+    check_decode(x, dtype, alpha, W, pattern)
