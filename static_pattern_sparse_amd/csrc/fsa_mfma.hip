@@ -85,8 +85,10 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int n_tiles, int* bh,
 // and V rows fit in half of the XCD's L2: the longest tiles of all the
 // group's heads then start first, and when every tile of a launch is
 // resident at once they no longer end last (forward 15.9 -> 14.9 us at
-// B8 H8 T1024, hg = 8; unchanged at B4 H8 T4096, hg = 2). The key-side and
-// dq kernels keep map_tile's order, which measured faster for them.
+// B8 H8 T1024, hg = 8; unchanged at B4 H8 T4096, hg = 2). dq takes pairs of
+// heads (21.8 -> 21.3 us at T1024, unchanged at T4096; groups of 4 and 8
+// measured slower); the key-side kernel keeps map_tile's order, which
+// measured fastest for it.
 __device__ __forceinline__ void map_tile_grouped(int bid, int BH, int n_tiles, int hg,
                                                  int* bh, int* tile) {
   if ((BH & 7) == 0 && hg > 1) {
@@ -744,7 +746,7 @@ template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, Problem pr, Taps taps, int n_tiles,
+    const float* __restrict__ lse, Problem pr, Taps taps, int n_tiles, int hg,
     float* __restrict__ dq, float* __restrict__ delta,
     float* __restrict__ partials) {
   using Tl = Tile<D>;
@@ -756,7 +758,7 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int T = pr.T, W = pr.W;
   int bh, tile;
-  map_tile(blockIdx.x, pr.B * pr.H, n_tiles, &bh, &tile);
+  map_tile_grouped(blockIdx.x, pr.B * pr.H, n_tiles, hg, &bh, &tile);
   const int i0 = tile * kTileQ;
   const size_t base = static_cast<size_t>(bh) * T * D;
   const uint32_t slab = static_cast<uint32_t>(T) * D * 2;
@@ -1167,16 +1169,22 @@ bool mfma_supported(const Problem& pr, int dtype) {
          pr.W <= 16 * (kMaxWinBlocks - 1) + 1;
 }
 
+// Heads interleaved per XCD by the query-side kernels: at most as many as
+// keep their K and V rows within half of the XCD's 4 MB L2, and at most
+// `cap`.
+static int head_group(const Problem& pr, int cap) {
+  const long long kv_head = 4LL * pr.T * pr.D;
+  const long long fit = (2LL << 20) / std::max(1LL, kv_head);
+  return static_cast<int>(std::max(1LL, std::min<long long>(
+      std::min<long long>((pr.B * pr.H) / 8, fit), cap)));
+}
+
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
                            const Problem& pr, const Taps& taps, void* out,
                            bool out_bf16, float* lse, hipStream_t s) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
-  // heads interleaved per XCD: as many as keep their K and V rows within
-  // half of the XCD's 4 MB L2
-  const long long kv_head = 4LL * pr.T * pr.D;
-  const int hg = static_cast<int>(std::max(1LL, std::min<long long>(
-      (pr.B * pr.H) / 8, (2LL << 20) / std::max(1LL, kv_head))));
+  const int hg = head_group(pr, 8);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
@@ -1214,16 +1222,17 @@ hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               float* delta, float* partials, hipStream_t s) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
+  const int hg = head_group(pr, 2);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   const auto* gg = static_cast<const uint16_t*>(dout);
   if (pr.D == 64)
     hipLaunchKernelGGL(bwd_dq_mfma_kernel<64>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, pr, taps, n_tiles, dq, delta, partials);
+                       gg, lse, pr, taps, n_tiles, hg, dq, delta, partials);
   else
     hipLaunchKernelGGL(bwd_dq_mfma_kernel<128>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, pr, taps, n_tiles, dq, delta, partials);
+                       gg, lse, pr, taps, n_tiles, hg, dq, delta, partials);
   return hipGetLastError();
 }
 
