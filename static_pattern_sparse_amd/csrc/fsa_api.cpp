@@ -195,8 +195,8 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
   return w;
 }
 
-// Kernel family: bf16 inputs with a window of at most 33 keys take the MFMA
-// tile kernels; fp32 inputs and wider windows take the lane-per-row kernels.
+// Kernel family: bf16 inputs take the MFMA tile kernels, fp32 inputs the
+// lane-per-row kernels.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const Taps& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s) {

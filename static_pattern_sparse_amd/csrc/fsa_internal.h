@@ -89,7 +89,7 @@ hipError_t launch_bwd_dkdv_vec(const void* q, const void* k, const void* v,
                                float* dv, hipStream_t s);
 size_t bwd_partials_used_vec(const Problem& pr);
 
-// MFMA tile kernels (fsa_mfma.hip): bf16 inputs, D in {64, 128}, W <= 33
+// MFMA tile kernels (fsa_mfma.hip): bf16 inputs, D in {64, 128}, any window
 bool mfma_supported(const Problem& pr, int dtype);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
                            const Problem& pr, const Taps& taps, void* out,

@@ -52,7 +52,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 constexpr int kTileQ = 15;          // queries per wavefront tile
 constexpr int kTileK = 14;          // key rows per dk/dv tile
-constexpr int kMaxWinBlocks = 3;    // window blocks: W <= 33
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -602,7 +601,9 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
   const bool qvalid = n < kTileQ && i < T;
   const float c2 = pr.scale * kLog2e;                 // scores in log2 units
   const LaneSel ls = lane_sel(n, g);
-  const int nwb = (W + kTileQ - 1) / 16 + 1;
+  // window blocks i0 - 16b: enough for the window (a window of T or more
+  // is the causal one), none wholly before row 0
+  const int nwb = min((min(W, T) + kTileQ - 1) / 16 + 1, (i0 + 15) / 16 + 1);
   const int nwp = (nwb + 1) / 2;
   const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
 
@@ -773,7 +774,9 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const float c2 = scale * kLog2e;
   const float L2 = qvalid ? lse[static_cast<size_t>(bh) * T + i] * kLog2e : 0.f;
   const LaneSel ls = lane_sel(n, g);
-  const int nwb = (W + kTileQ - 1) / 16 + 1;
+  // window blocks i0 - 16b: enough for the window (a window of T or more
+  // is the causal one), none wholly before row 0
+  const int nwb = min((min(W, T) + kTileQ - 1) / 16 + 1, (i0 + 15) / 16 + 1);
   const int nwp = (nwb + 1) / 2;
   const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
 
@@ -1006,7 +1009,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) dalpha[0] = static_cast<float>(acc);
   }
-  const int nqb = (W + kTileK + 15) / 16;              // window query blocks
+  // window query blocks rowb + 16b: enough for the window, none wholly past
+  // the last row
+  const int nqb = min((min(W, T) + kTileK + 15) / 16, (T - rowb + 15) / 16);
   const int nwp = (nqb + 1) / 2;
   int ntap = 0;                                         // taps with a query < T
   while (ntap < taps.n && taps.c[ntap] <= T - j0) ++ntap;
@@ -1164,9 +1169,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 
 }  // namespace
 
 bool mfma_supported(const Problem& pr, int dtype) {
-  // the window of query i0 reaches back W-1 rows: ceil((W-1)/16) + 1 blocks
-  return dtype == FSA_DTYPE_BF16 && (pr.D == 64 || pr.D == 128) &&
-         pr.W <= 16 * (kMaxWinBlocks - 1) + 1;
+  return dtype == FSA_DTYPE_BF16 && (pr.D == 64 || pr.D == 128);
 }
 
 // Heads interleaved per XCD by the query-side kernels: at most as many as

@@ -130,8 +130,11 @@ SMALL = [
     (1, 2, 250, 64, "bf16", 1.0, 300),          # W > T: causal attention
     (1, 1, 200, 128, "f32", 0.8333333, 12),
     (1, 1, 64, 64, "bf16", 1.0, 1),
-    (1, 2, 700, 64, "bf16", 0.6333333, 33),     # widest window of the tile kernels
-    (1, 1, 700, 128, "bf16", 0.6333333, 34),    # first window past them
+    (1, 2, 700, 64, "bf16", 0.6333333, 33),     # three window blocks per tile
+    (1, 1, 700, 128, "bf16", 0.6333333, 34),
+    (1, 2, 700, 64, "bf16", 0.6333333, 64),     # wide windows: several window pairs
+    (2, 1, 500, 128, "bf16", 1.1, 100),
+    (1, 2, 300, 64, "bf16", 0.9, 5000),         # W far past T: causal attention
     (2, 1, 29, 64, "bf16", 1.1, 2),
 ]
 

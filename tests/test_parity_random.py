@@ -2,7 +2,7 @@
 the fp64 oracle, forward and backward, through the C ABI.
 
 The draws cover ragged tails (T not a multiple of the 15-query or 14-key
-tiles), windows on both sides of the tile kernels' limit (33), head dims 64
+tiles), windows of one to five window blocks (1-69 keys), head dims 64
 and 128, both input dtypes and all four tap patterns; a second set draws
 sequences of 700-3200 rows, where the longest taps reach back inside the
 slab. Tolerances as in test_parity.
