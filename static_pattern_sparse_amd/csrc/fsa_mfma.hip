@@ -946,8 +946,10 @@ __device__ __forceinline__ TapSel key_tap_sel(int n, int g) {
   return TapSel{code[0] | (code[1] << 16), code[2] | (code[3] << 16)};
 }
 
+// Register budget: five wavefronts per SIMD at D = 64 (96 VGPRs), three at
+// D = 128 (164 VGPRs; two, at 171, took 5-8% longer at T = 65536).
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1))) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 3))) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
