@@ -22,6 +22,8 @@ slows the launch that follows.
 
 value = layers * B * H * T / step time (token-heads per second, every layer
 counted). The JSON line also carries:
+  pass_tokens_heads_per_s  the forward and the backward (both stages) each
+                as B*H*T over its event-timed mean per layer;
   copy_gbs      a plain 1 GiB device copy's read+write GB/s, for context;
   roofline      the dominant kernel's algorithmic bytes per launch divided by
                 its mean event-to-event launch time, against the 8 TB/s HBM
@@ -373,7 +375,9 @@ def summarise(stack, ms_step, per_ms):
                          / 1e9 / HBM_PEAK_GBS, 4),
     }
     value = stack.layers * th / (ms_step * 1e-3)
-    return value, kernels, frac
+    # the forward and the backward timed separately (event means per layer)
+    passes = {"fwd": round(th / (fwd_ms * 1e-3), 1), "bwd": round(th / (bwd_ms * 1e-3), 1)}
+    return value, kernels, frac, passes
 
 
 def source_digest():
@@ -518,7 +522,7 @@ def main():
     stack = Stack(wl, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
     print(f"[bench] {wl.name}: {args.layers} layers resident", file=sys.stderr, flush=True)
     ms_step, per_ms, counts = time_stack(stack, args.steps, args.warmup, torch)
-    value, kernels, frac = summarise(stack, ms_step, per_ms)
+    value, kernels, frac, passes = summarise(stack, ms_step, per_ms)
     print(f"[bench] {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     dom = max(per_ms, key=lambda n: per_ms[n])
@@ -546,6 +550,7 @@ def main():
                    "pass": "forward+backward"},
         "roofline": roofline,
         "hbm_frac": frac,
+        "pass_tokens_heads_per_s": passes,
         # context: a plain 1 GiB device copy on the same GPU (read + write)
         "copy_gbs": copy_bandwidth(torch),
         "kernels": kernels,
@@ -559,9 +564,10 @@ def main():
         st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
         print(f"[bench] {wl2.name} W=12 resident", file=sys.stderr, flush=True)
         ms2, per2, _ = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
-        v2, k2, f2 = summarise(st2, ms2, per2)
+        v2, k2, f2, p2 = summarise(st2, ms2, per2)
         res["t4096"] = {"workload": wl2.name + " (W=12)", "value": round(v2, 1),
-                        "ms_per_step": round(ms2, 4), "hbm_frac": f2, "kernels": k2}
+                        "ms_per_step": round(ms2, 4), "hbm_frac": f2,
+                        "pass_tokens_heads_per_s": p2, "kernels": k2}
         # the window sweep of the same stack: forward launches only (the
         # inputs do not depend on W), host clock over back-to-back launches
         sweep = {}
@@ -591,10 +597,10 @@ def main():
         st4 = Stack(wl4, 12, 1, torch, F, I, args.pattern, args.out_bf16)
         print(f"[bench] {wl4.name} (one layer) resident", file=sys.stderr, flush=True)
         ms4, per4, _ = time_stack(st4, max(2, args.steps // 2), 1, torch)
-        v4, k4, f4 = summarise(st4, ms4, per4)
+        v4, k4, f4, p4 = summarise(st4, ms4, per4)
         res["t65536"] = {"workload": wl4.name + " (one layer, alpha of layer 0)",
                          "value": round(v4, 1), "ms_per_step": round(ms4, 4),
-                         "hbm_frac": f4, "kernels": k4}
+                         "hbm_frac": f4, "pass_tokens_heads_per_s": p4, "kernels": k4}
         del st4
         torch.cuda.empty_cache()
 
