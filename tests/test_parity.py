@@ -306,7 +306,7 @@ def _sample_rows(T, alpha, W, seed):
     return np.array(sorted(r for r in rows if 0 <= r < T))
 
 
-@pytest.mark.parametrize("layer", [0, 15])
+@pytest.mark.parametrize("layer", [0, 7, 15])
 def test_workload_long_t65536_sampled(layer):
     """Full-size long-sequence layer: every output row sampled at the edges and
     around every tap distance is checked one by one; dalpha is checked against
@@ -344,7 +344,7 @@ def test_workload_long_t65536_sampled(layer):
 
 # ------------------------------------------------------------------ bf16 output
 BF16_OUT_CASES = [
-    # B, H, T, D, dtype, alpha, W  (tile kernels, then lane-per-row kernels)
+    # B, H, T, D, dtype, alpha, W  (bf16: tile kernels; f32: lane-per-row kernels)
     (2, 2, 700, 64, "bf16", 0.7317, 12),
     (1, 2, 333, 128, "bf16", 1.2913, 6),
     (1, 1, 300, 64, "f32", 0.9, 5),
