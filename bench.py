@@ -58,6 +58,7 @@ import math
 import multiprocessing
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -106,9 +107,11 @@ class Stack:
         B, H, T, D = wl.B, wl.H, wl.T, wl.D
         dev = "cuda"
         self.L = []
+        self.host = []                 # the layers' host inputs (oracle checks)
         ws_bytes = F.fsa_backward_workspace_size(B, H, T, D, F.FSA_DTYPE_BF16)
         for l in range(layers):
             x = I.workload_inputs(wl, l)
+            self.host.append(x)
             t = {n: I.to_device(x[n], wl.dtype) for n in ("q", "k", "v", "dout")}
             f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
             t.update(out=torch.empty((B, H, T, D), dtype=out_dt, device=dev),
@@ -117,6 +120,24 @@ class Stack:
                      ws=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev))
             self.L.append(t)
         self._prepare_calls(torch, F)
+
+    def snapshot(self, check_layers):
+        """What the oracle checks need once the device buffers are freed: the
+        host inputs, the alphas and the GPU results of `check_layers`."""
+        import types
+        return types.SimpleNamespace(
+            wl=self.wl, layers=self.layers, W=self.W, alphas=self.alphas,
+            out_bytes=self.out_bytes, host=self.host,
+            got={l: self.results(l) for l in check_layers},
+            da={l: self.dalpha(l) for l in check_layers})
+
+    def results(self, l):
+        """Layer l's GPU results as host float32 arrays."""
+        t = self.L[l]
+        return {n: t[n].float().cpu().numpy() for n in ("out", "lse", "dq", "dk", "dv")}
+
+    def dalpha(self, l):
+        return float(self.L[l]["dalpha"].item())
 
     def _prepare_calls(self, torch, F):
         """Pre-marshal every launch of a step (raw ctypes argument tuples), so
@@ -313,17 +334,25 @@ class Events:
             raise RuntimeError("hipEventRecord failed")
         self.marks.append((name, e))
 
-    def per_kernel_ms(self):
-        tot, cnt = {}, {}
+    def per_kernel_ms(self, skip_steps=1):
+        """Median event-to-event time of each kernel over the recorded steps
+        after the first `skip_steps` ones, and the launches counted. The
+        median, not the mean: a host stall that drains the queue lands in
+        whichever gap it falls in and would move a mean by its whole length."""
+        gaps = {}
         f = self.ct.c_float()
+        step = 0
         for (name, e0), (_, e1) in zip(self.marks, self.marks[1:]):
             if name is None:
+                step += 1
+                continue
+            if step < skip_steps:
                 continue
             if self.hip.hipEventElapsedTime(self.ct.byref(f), e0, e1) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
-            tot[name] = tot.get(name, 0.0) + f.value
-            cnt[name] = cnt.get(name, 0) + 1
-        return {n: tot[n] / cnt[n] for n in tot}, cnt
+            gaps.setdefault(name, []).append(f.value)
+        med = {n: statistics.median(v) for n, v in gaps.items()}
+        return med, {n: len(v) for n, v in gaps.items()}
 
     def close(self):
         for e in self.pool:
@@ -333,7 +362,9 @@ class Events:
 
 def time_stack(stack, steps, warmup, torch):
     """Step time on the host clock with no events between launches; then the
-    per-kernel event times over as many steps again."""
+    per-kernel event medians over as many steps again (one more step is run
+    first and dropped). Returns (ms per step, median ms per kernel, launches
+    per step per kernel)."""
     for _ in range(warmup):
         stack.step()
     torch.cuda.synchronize()
@@ -343,13 +374,25 @@ def time_stack(stack, steps, warmup, torch):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    ev = Events(torch, steps * (len(stack.order) + 1))
-    for _ in range(steps):
+    ev = Events(torch, (steps + 1) * (len(stack.order) + 1))
+    for _ in range(steps + 1):
         stack.step(ev)
     torch.cuda.synchronize()
-    per_ms, counts = ev.per_kernel_ms()
+    per_ms, counts = ev.per_kernel_ms(skip_steps=1)
     ev.close()
-    return ms_step, per_ms, counts
+    per_step = {n: c // steps for n, c in counts.items()}
+    return ms_step, per_ms, per_step
+
+
+def consistency(ms_step, per_ms, per_step):
+    """Self-check of the per-kernel figures: the kernel medians times their
+    launches per step, summed, against the host-clock step time. The two
+    measure the same launches (the event gaps include the gaps between
+    kernels), so they must agree; a ratio outside 0.9-1.1 flags the line."""
+    total = sum(per_ms[n] * per_step[n] for n in per_ms)
+    ratio = total / ms_step if ms_step > 0 else float("nan")
+    return {"sum_kernel_ms": round(total, 4), "ms_per_step": round(ms_step, 4),
+            "ratio": round(ratio, 4), "ok": bool(0.9 <= ratio <= 1.1)}
 
 
 def summarise(stack, ms_step, per_ms):
@@ -360,7 +403,7 @@ def summarise(stack, ms_step, per_ms):
     ab = algo_bytes(wl.D, in_b, stack.out_bytes)
     kernels = {}
     for n, ms in per_ms.items():
-        k = {"mean_us": round(ms * 1e3, 3)}
+        k = {"median_us": round(ms * 1e3, 3)}
         if n in sb:
             gbs = sb[n] * th / (ms * 1e-3) / 1e9
             k.update(bytes_per_launch=sb[n] * th, gbs=round(gbs, 1),
@@ -388,18 +431,21 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, per_launch_tokens):
+def load_traffic(kernel, per_launch_tokens, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary of the
-    kernel, when it was taken on the current kernel source; else None."""
+    kernel on `workload`, when it was taken on the current kernel source; else
+    None. The summary holds one line per workload:
+        hbm_bytes_per_token_head <workload>: <bytes>"""
     path = os.path.join(PROFILES, f"traffic_{kernel}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source_digest:\s*(\w+)", text)
-    b = re.search(r"hbm_bytes_per_token_head:\s*([0-9.eE+-]+)", text)
+    b = re.search(r"hbm_bytes_per_token_head\s+" + re.escape(workload)
+                  + r":\s*([0-9.eE+-]+)", text)
     if not m or not b or m.group(1) != source_digest():
         return None
-    return float(b.group(1)) * per_launch_tokens
+    return round(float(b.group(1)) * per_launch_tokens)
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
@@ -424,54 +470,117 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
 
 
 # ------------------------------------------------------------- CPU baseline
+TOL_MAX_ABS = {"bf16": 2e-3, "f32": 2e-5}
+TOL_DALPHA_REL = 1e-3
+
+
 def _oracle_layer(args):
+    """The fp64 oracle's forward and backward over every (b, h) slab of one
+    layer; when the GPU results of the layer are given, also their largest
+    absolute difference from the oracle per output, and the oracle's dalpha
+    (summed in a fixed order)."""
     import numpy as np
     from oracle import fsa_oracle as O
-    q, k, v, g, alpha, W, base, mode = args
+    q, k, v, g, alpha, W, base, mode, got = args
     B, H = q.shape[:2]
-    t0 = time.perf_counter()
+    errs = {n: 0.0 for n in ("out", "lse", "dq", "dk", "dv")}
+    parts = []
+    busy = 0.0
     for b in range(B):
         for h in range(H):
+            t0 = time.perf_counter()
             sl = [x[b, h].astype(np.float64) for x in (q, k, v, g)]
-            O.forward_slab(sl[0], sl[1], sl[2], alpha, W, base=base, mode=mode)
-            O.backward_slab(sl[0], sl[1], sl[2], sl[3], alpha, W, base=base,
-                            mode=mode)
-    return time.perf_counter() - t0
+            ro, rl = O.forward_slab(sl[0], sl[1], sl[2], alpha, W, base=base, mode=mode)
+            rq, rk, rv, ra, _ = O.backward_slab(sl[0], sl[1], sl[2], sl[3], alpha, W,
+                                                base=base, mode=mode)
+            busy += time.perf_counter() - t0
+            parts.append(ra)
+            if got is not None:
+                for n, r in (("out", ro), ("lse", rl), ("dq", rq), ("dk", rk), ("dv", rv)):
+                    e = float(np.abs(got[n][b, h].astype(np.float64) - r).max())
+                    errs[n] = max(errs[n], e)
+    return busy, (errs if got is not None else None), math.fsum(parts)
 
 
 def _noop(_):
     return os.getpid()
 
 
-def cpu_baseline(wl, window, alphas, layers, pattern="fib", passes=2):
-    """The fp64 oracle (forward + backward of every (b, h) slab) over whole
-    layers of the workload, one layer per worker task, `passes` times over the
-    step (about 15 s of CPU work in all)."""
-    from static_pattern_sparse_amd import inputs as I
+def cpu_baseline(stack, pattern="fib", passes=2):
+    """The fp64 oracle (forward + backward of every (b, h) slab) over every
+    layer of the stack, one layer per worker task, `passes` times over the
+    step; timed as a reported baseline. On its first pass the results of the
+    layers whose GPU results the snapshot holds are compared with them
+    (outside any timed GPU region). `stack` is a Stack.snapshot()."""
+    wl, layers = stack.wl, stack.layers
+    check_layers = tuple(stack.got)
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
+    base, _, mode = pattern.partition("-")
+    mode = "round" if mode == "round" else "lerp"
     jobs = []
-    for l in range(layers):
-        x = I.workload_inputs(wl, l)
-        base, _, mode = pattern.partition("-")
-        jobs.append((x["q"], x["k"], x["v"], x["dout"], float(alphas[l]), window,
-                     base, "round" if mode == "round" else "lerp"))
+    for p in range(passes):
+        for l in range(layers):
+            x = stack.host[l]
+            got = stack.got[l] if (p == 0 and l in check_layers) else None
+            jobs.append((x["q"], x["k"], x["v"], x["dout"], float(stack.alphas[l]),
+                         stack.W, base, mode, got))
     ctx = multiprocessing.get_context("spawn")
     from concurrent.futures import ProcessPoolExecutor
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
         list(ex.map(_noop, range(workers * 2)))          # start every worker
         t0 = time.perf_counter()
-        busy = list(ex.map(_oracle_layer, jobs * passes))
+        res = list(ex.map(_oracle_layer, jobs))
         wall = time.perf_counter() - t0
     th = passes * layers * wl.B * wl.H * wl.T
-    return {"value": round(th / wall, 1), "unit": "tokens·heads/s",
-            "cores": workers, "kind": "oracle",
-            "sample": (f"{passes} passes over {layers} layers x {wl.B * wl.H} (b,h) "
-                       f"slabs of {wl.name}, "
-                       f"forward+backward in fp64 numpy, {workers} spawned "
-                       f"single-threaded workers; {wall:.1f} s wall, "
-                       f"{sum(busy):.1f} s CPU")}
+    base_line = {"value": round(th / wall, 1), "unit": "tokens·heads/s",
+                 "cores": workers, "kind": "oracle",
+                 "sample": (f"{passes} passes over {layers} layers x {wl.B * wl.H} (b,h) "
+                            f"slabs of {wl.name} (W={stack.W}), forward+backward in "
+                            f"fp64 numpy, {workers} spawned single-threaded workers; "
+                            f"{wall:.1f} s wall, {sum(r[0] for r in res):.1f} s CPU")}
+    parity = None
+    if check_layers:
+        errs = {n: 0.0 for n in ("out", "lse", "dq", "dk", "dv")}
+        da_rel = 0.0
+        for l, r in zip(range(layers), res[:layers]):
+            if l not in check_layers:
+                continue
+            for n in errs:
+                errs[n] = max(errs[n], r[1][n])
+            got_da = stack.da[l]
+            if r[2] != 0.0:
+                da_rel = max(da_rel, abs(got_da - r[2]) / abs(r[2]))
+            elif got_da != 0.0:
+                da_rel = float("inf")
+        tol = TOL_MAX_ABS[wl.dtype]
+        out_ok = stack.out_bytes == 4
+        parity = {"layers": sorted(check_layers), "max_abs": {n: float(f"{e:.3g}") for n, e in errs.items()},
+                  "dalpha_rel": float(f"{da_rel:.3g}"),
+                  "tol": {"max_abs": tol, "dalpha_rel": TOL_DALPHA_REL},
+                  "ok": bool(all(e <= tol for n, e in errs.items() if n != "out" or out_ok)
+                             and da_rel <= TOL_DALPHA_REL)}
+    return base_line, parity
+
+
+# ------------------------------------------------------------- roofline
+def roofline(stack, per_ms, kernels, traffic_ok):
+    """Roofline object of the dominant kernel (the longest median launch):
+    its algorithmic bytes per launch over that median, against the 8 TB/s HBM
+    peak; traffic from the committed counter summary when it was taken on the
+    current kernel source and workload, else null."""
+    wl = stack.wl
+    th = wl.B * wl.H * wl.T
+    dom = max((n for n in per_ms if n in kernels and "gbs" in kernels[n]),
+              key=lambda n: per_ms[n])
+    achieved = kernels[dom]["gbs"]
+    traffic = load_traffic(dom, th, wl.name) if traffic_ok else None
+    return {"bound": "hbm", "kernel": dom, "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": kernels[dom]["bytes_per_launch"],
+            "median_launch_us": kernels[dom]["median_us"]}
 
 
 # ------------------------------------------------------------- main
@@ -525,17 +634,9 @@ def main():
     value, kernels, frac, passes = summarise(stack, ms_step, per_ms)
     print(f"[bench] {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
-    dom = max(per_ms, key=lambda n: per_ms[n])
-    th = wl.B * wl.H * wl.T
-    achieved = kernels[dom]["gbs"]
     # the committed counter summaries were taken with the Fibonacci table
-    traffic = (load_traffic(dom, th)
-               if args.pattern == "fib" and not args.out_bf16 else None)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": kernels[dom]["bytes_per_launch"],
-                "mean_launch_us": kernels[dom]["mean_us"]}
+    traffic_ok = args.pattern == "fib" and not args.out_bf16
+    roof = roofline(stack, per_ms, kernels, traffic_ok)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens·heads/s",
@@ -548,14 +649,18 @@ def main():
                    "pattern": args.pattern,
                    "out_dtype": "bf16" if args.out_bf16 else "f32",
                    "pass": "forward+backward"},
-        "roofline": roofline,
+        "roofline": roof,
+        "consistency": consistency(ms_step, per_ms, counts),
         "hbm_frac": frac,
         "pass_tokens_heads_per_s": passes,
         # context: a plain 1 GiB device copy on the same GPU (read + write)
         "copy_gbs": copy_bandwidth(torch),
         "kernels": kernels,
-        "launches_per_kernel": counts,
+        "launches_per_step": counts,
     }
+    # the first and the last layer's GPU results, for the oracle check that
+    # runs with the CPU baseline after every GPU leg
+    snap1024 = stack.snapshot((0, args.layers - 1)) if not args.no_cpu_baseline else None
     del stack
     torch.cuda.empty_cache()
 
@@ -563,11 +668,16 @@ def main():
         wl2 = I.WORKLOADS["coprime16_bf16_b4h8t4096d64_w6-12"]
         st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
         print(f"[bench] {wl2.name} W=12 resident", file=sys.stderr, flush=True)
-        ms2, per2, _ = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
+        ms2, per2, cnt2 = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
         v2, k2, f2, p2 = summarise(st2, ms2, per2)
         res["t4096"] = {"workload": wl2.name + " (W=12)", "value": round(v2, 1),
-                        "ms_per_step": round(ms2, 4), "hbm_frac": f2,
+                        "ms_per_step": round(ms2, 4),
+                        "roofline": roofline(st2, per2, k2, traffic_ok),
+                        "consistency": consistency(ms2, per2, cnt2),
+                        "hbm_frac": f2,
                         "pass_tokens_heads_per_s": p2, "kernels": k2}
+        snap4096 = (st2.snapshot((1, args.layers - 1))
+                    if not args.no_cpu_baseline else None)
         # the window sweep of the same stack: forward launches only (the
         # inputs do not depend on W), host clock over back-to-back launches
         sweep = {}
@@ -596,10 +706,11 @@ def main():
         wl4 = I.WORKLOADS["linear16_bf16_b1h16t65536d128_w12"]
         st4 = Stack(wl4, 12, 1, torch, F, I, args.pattern, args.out_bf16)
         print(f"[bench] {wl4.name} (one layer) resident", file=sys.stderr, flush=True)
-        ms4, per4, _ = time_stack(st4, max(2, args.steps // 2), 1, torch)
+        ms4, per4, cnt4 = time_stack(st4, max(2, args.steps // 2), 1, torch)
         v4, k4, f4, p4 = summarise(st4, ms4, per4)
         res["t65536"] = {"workload": wl4.name + " (one layer, alpha of layer 0)",
                          "value": round(v4, 1), "ms_per_step": round(ms4, 4),
+                         "consistency": consistency(ms4, per4, cnt4),
                          "hbm_frac": f4, "pass_tokens_heads_per_s": p4, "kernels": k4}
         del st4
         torch.cuda.empty_cache()
@@ -618,7 +729,7 @@ def main():
             "us_per_step": round(ms3 * 1e3, 2),
             "tokens_per_s": round(wl3.B / (ms3 * 1e-3), 1),
             "graph_us_per_step": round(graph_ms * 1e3, 2),
-            "mean_launch_us": round(launch_us, 3),
+            "median_launch_us": round(launch_us, 3),
             "algorithmic_bytes_per_launch": int(nbytes),
             "gbs": round(nbytes / (launch_us * 1e-6) / 1e9, 1),
             "bound": "latency"}
@@ -638,7 +749,7 @@ def main():
             for name, nbytes in (("rope", elems * (2 + 2)), ("rope_inv", elems * (4 + 4))):
                 us = per5[name] * 1e3
                 gbs = nbytes / (us * 1e-6) / 1e9
-                rope[name] = {"mean_launch_us": round(us, 3),
+                rope[name] = {"median_launch_us": round(us, 3),
                               "algorithmic_bytes_per_launch": nbytes,
                               "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
             res["rope"][key] = rope
@@ -646,9 +757,12 @@ def main():
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, 12, F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 16),
-                                           args.layers, args.pattern)
+        print("[bench] cpu baseline and oracle check", file=sys.stderr, flush=True)
+        res["cpu_baseline"], res["parity"] = cpu_baseline(snap1024, args.pattern, passes=2)
+        if not args.skip_t4096:
+            cb, par = cpu_baseline(snap4096, args.pattern, passes=1)
+            res["t4096"]["cpu_baseline"] = cb
+            res["t4096"]["parity"] = par
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

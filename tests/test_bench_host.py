@@ -34,16 +34,29 @@ def test_traffic_summary_follows_the_kernel_source():
     current kernel sources."""
     digest = bench.source_digest()
     assert len(digest) == 16
+    wl = "linear16_bwd_bf16_b8h8t1024d64_w12"
     for k in ("fwd", "bwd_dq", "bwd_dkdv"):
         path = os.path.join(bench.PROFILES, f"traffic_{k}.txt")
         assert os.path.exists(path), path
         text = open(path).read()
         if f"source_digest: {digest}" in text:
-            v = bench.load_traffic(k, 1000)
+            v = bench.load_traffic(k, 1000, wl)
             assert v is not None and v > 0
         else:
-            assert bench.load_traffic(k, 1000) is None
-    assert bench.load_traffic("no_such_kernel", 1000) is None
+            assert bench.load_traffic(k, 1000, wl) is None
+        assert bench.load_traffic(k, 1000, "no_such_workload") is None
+    assert bench.load_traffic("no_such_kernel", 1000, wl) is None
+
+
+def test_consistency_flag():
+    """The self-check compares the kernel medians times their launches with
+    the host-clock step time and flags a disagreement beyond 10%."""
+    per_ms = {"fwd": 0.015, "bwd_dq": 0.022, "bwd_dkdv": 0.023}
+    per_step = {"fwd": 16, "bwd_dq": 16, "bwd_dkdv": 16}
+    ok = bench.consistency(0.96, per_ms, per_step)
+    assert ok["ok"] and abs(ok["sum_kernel_ms"] - 0.96) < 1e-9
+    bad = bench.consistency(0.96, dict(per_ms, fwd=0.138), per_step)
+    assert not bad["ok"] and bad["ratio"] > 1.1
 
 
 def test_more_than_one_gpu_is_refused():
