@@ -7,4 +7,6 @@ from .fsa_oracle import (BASES, FIB, MODES, POW2, SCHEDULE_COPRIME,  # noqa: F40
                          SCHEDULE_FIXED, TapTable,
                          SCHEDULE_LINEAR, backward, backward_slab, decode, dkdv_rows,
                          dq_rows, forward, forward_rows, forward_slab,
-                         offset_table, rope, schedule)
+                         offset_table, rope, schedule, OPT_ADAM, OPT_SGD, THETA_CLAMP,
+                         THETA_TANH, alpha_of_theta, dalpha_dtheta, theta_init,
+                         theta_step, theta_to_alpha)

@@ -49,6 +49,17 @@ Readings taken where the page leaves a step open:
   4096 tokens (1024, 2048; Core contributions and results > 3. Length
   extrapolation, base sensitivity) need a ladder past 987, and fifteen terms
   match the Fibonacci list's count.
+* R16 learned alpha (Methodology > Experimental variables, Learned): one free
+  parameter theta per layer, initialised so that alpha = 1, trained by
+  gradient descent, alpha held in [0.5, 1.5] (Architecture and attention >
+  Scaling). The page names neither the map from theta to alpha nor the
+  optimizer. Two maps are provided: "clamp", alpha = clip(theta, 0.5, 1.5)
+  with theta projected back into [0.5, 1.5] after every update (projected
+  gradient descent; theta starts at 1), and "tanh", alpha = 1 + tanh(theta)/2
+  with theta unconstrained (theta starts at 0). alpha is evaluated in fp64 and
+  rounded once to fp32 (reading R7); the chain rule takes the rounding as the
+  identity, dL/dtheta = dL/dalpha * dalpha/dtheta. Optimizers: plain gradient
+  descent, theta <- theta - lr * g, and Adam with bias correction.
 * R15 the rounded (mask) mode of the static runs (Core contributions and
   results > 2. Learned dilation is inert, efficiency) attends row i - round(d_k)
   with round to nearest, ties to even; a term is kept under the same rule
@@ -536,3 +547,83 @@ def rope(x, base, pos0=None, inverse=False):
         y[b, :, :, :half] = lo * c - hi * s
         y[b, :, :, half:] = lo * s + hi * c
     return y
+
+
+# ---------------------------------------------------------------------------
+# learned alpha: theta -> alpha, its slope, and the optimizer step (reading R16)
+# [DSFS: Methodology > Experimental variables, Learned; Architecture and
+# attention > Scaling (alpha in [0.5, 1.5])]
+# ---------------------------------------------------------------------------
+THETA_CLAMP = 0
+THETA_TANH = 1
+OPT_SGD = 0
+OPT_ADAM = 1
+ALPHA_MIN, ALPHA_MAX = 0.5, 1.5
+
+
+def theta_init(theta_map: int) -> float:
+    """The theta at which alpha = 1 (the page initialises the learned scalar
+    there)."""
+    return 1.0 if theta_map == THETA_CLAMP else 0.0
+
+
+def theta_to_alpha(theta: float, theta_map: int) -> float:
+    """alpha(theta) in fp64: clip(theta, 0.5, 1.5), or 1 + tanh(theta)/2."""
+    t = float(theta)
+    if theta_map == THETA_CLAMP:
+        return min(max(t, ALPHA_MIN), ALPHA_MAX)
+    if theta_map == THETA_TANH:
+        return 1.0 + 0.5 * math.tanh(t)
+    raise ValueError("unknown theta map")
+
+
+def alpha_of_theta(theta: float, theta_map: int) -> float:
+    """The fp32 alpha the attention layer uses: alpha(theta) rounded once."""
+    return float(np.float32(theta_to_alpha(theta, theta_map)))
+
+
+def dalpha_dtheta(theta: float, theta_map: int) -> float:
+    """Slope of the map: 1 on the closed interval [0.5, 1.5] and 0 outside it
+    for the clip; (1 - tanh(theta)^2) / 2 for the tanh map."""
+    t = float(theta)
+    if theta_map == THETA_CLAMP:
+        return 1.0 if ALPHA_MIN <= t <= ALPHA_MAX else 0.0
+    if theta_map == THETA_TANH:
+        th = math.tanh(t)
+        return 0.5 * (1.0 - th * th)
+    raise ValueError("unknown theta map")
+
+
+def theta_step(theta, dalpha, m, v, step, theta_map, optimizer, lr,
+               beta1=0.9, beta2=0.999, eps=1e-8):
+    """One optimizer update of every layer's theta from the layers' dL/dalpha.
+
+    g_l = dalpha_l * dalpha/dtheta(theta_l) (chain rule, reading R16);
+      gradient descent:  theta_l <- theta_l - lr * g_l;
+      Adam (1-based step t = step + 1):
+        m_l <- beta1 m_l + (1 - beta1) g_l,  v_l <- beta2 v_l + (1 - beta2) g_l^2,
+        theta_l <- theta_l - lr * (m_l / (1 - beta1^t)) / (sqrt(v_l / (1 - beta2^t)) + eps);
+    with the clip map theta is then projected onto [0.5, 1.5].
+    Arguments are sequences over layers (fp32 values), step the number of
+    updates already made. Returns (theta, m, v, g) as fp64 arrays; the
+    library stores theta, m and v in fp32.
+    """
+    th = np.asarray(theta, dtype=np.float64).copy()
+    da = np.asarray(dalpha, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64).copy()
+    v = np.asarray(v, dtype=np.float64).copy()
+    g = np.array([da[l] * dalpha_dtheta(th[l], theta_map) for l in range(len(th))])
+    if optimizer == OPT_SGD:
+        th = th - lr * g
+    elif optimizer == OPT_ADAM:
+        t = int(step) + 1
+        m = beta1 * m + (1.0 - beta1) * g
+        v = beta2 * v + (1.0 - beta2) * g * g
+        mh = m / (1.0 - beta1 ** t)
+        vh = v / (1.0 - beta2 ** t)
+        th = th - lr * mh / (np.sqrt(vh) + eps)
+    else:
+        raise ValueError("unknown optimizer")
+    if theta_map == THETA_CLAMP:
+        th = np.clip(th, ALPHA_MIN, ALPHA_MAX)
+    return th, m, v, g
