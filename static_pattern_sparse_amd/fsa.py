@@ -67,6 +67,10 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m static_pattern_sparse_amd.build_lib`")
+    # torch first: its HIP runtime is then the one libfsa binds to (same
+    # soname). Loaded the other way round, the process would hold two HIP
+    # runtimes, and torch's streams and memory would be foreign to libfsa's.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.fsa_schedule.argtypes = [i32, i32, f32, f32, i32, ctypes.POINTER(f32)]
