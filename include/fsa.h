@@ -38,7 +38,10 @@
  * inside kernels surface later, at the caller's synchronisation.
  *
  * Thread safety: the library holds no mutable global state apart from the
- * thread-local last HIP error; calls from several threads are safe.
+ * thread-local last HIP error and fsa_backward_noalloc's per-device scratch
+ * address (looked up once under a lock); calls from several threads are safe,
+ * except fsa_backward_noalloc calls that overlap on one GPU (they share its
+ * scratch array).
  */
 #ifndef FSA_H_
 #define FSA_H_
@@ -56,6 +59,7 @@ extern "C" {
 #define FSA_ERR_UNSUPPORTED 2 /* head dim, dtype or size with no kernel */
 #define FSA_ERR_WORKSPACE 3   /* workspace missing or smaller than required */
 #define FSA_ERR_HIP 4         /* a HIP launch failed; see fsa_last_hip_error() */
+#define FSA_ERR_SCRATCH 5     /* beyond fsa_backward_noalloc's fixed scratch */
 
 /* schedules [DSFS: Methodology > Experimental variables] */
 #define FSA_SCHEDULE_FIXED 0   /* alpha = 1 for every layer */
@@ -235,6 +239,30 @@ int fsa_backward_dkdv_ex(const void* q, const void* k, const void* v,
                          int pattern, float* dk, float* dv, float* dalpha,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * fsa_backward_noalloc -- fsa_backward_ex with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Arguments, layouts, results and errors as fsa_backward_ex. The per-row
+ *   softmax terms and the per-tile dalpha partials go to a fixed device array
+ *   of FSA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ *   on until the process ends (looked up at the first call on each device;
+ *   the device is the stream's). A problem whose fsa_backward_workspace_size
+ *   exceeds it returns FSA_ERR_SCRATCH before any HIP call (16 MiB covers
+ *   B*H*T up to about 1.9 million rows, e.g. B1 H16 T65536 at D = 128).
+ *   The array keeps the last call's contents; every element the kernels read
+ *   is written earlier in the same call, so nothing is cleared. All calls on
+ *   one GPU share the array: calls that overlap in time on one GPU (two
+ *   streams, two threads) race and give wrong results; serialise them.
+ *   The call itself allocates nothing (no hipMalloc, no library allocation).
+ */
+#define FSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fsa_backward_noalloc(const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, int dtype, int B,
+                         int H, int T, int D, float alpha, int window,
+                         int pattern, float* dq, float* dk, float* dv,
+                         float* dalpha, void* stream);
 
 /*
  * fsa_decode -- one decoding step: a new query per (b, h) against the cached

@@ -235,6 +235,26 @@ size_t bwd_partials_used(const Problem& pr, int dtype) {
                                    : bwd_partials_used_vec(pr);
 }
 
+int check_backward_call(const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, int dtype, int B,
+                        int H, int T, int D, float alpha, int window,
+                        int pattern, const float* dq, const float* dk,
+                        const float* dv, const float* dalpha, bool* empty) {
+  if (!pattern_ok(pattern)) return FSA_ERR_INVALID_ARG;
+  int st = check_shape(dtype, B, H, T, D, alpha, window);
+  if (st != FSA_OK) return st;
+  if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
+  *empty = static_cast<long long>(B) * H * T == 0;
+  if (*empty) return FSA_OK;
+  if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv) return FSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FSA_ERR_INVALID_ARG;
+  return FSA_OK;
+}
+
+int status_of(hipError_t e) { return hip_status(e); }
+
 }  // namespace fsa
 
 using namespace fsa;
@@ -364,14 +384,14 @@ int fsa_backward_ex(const void* q, const void* k, const void* v,
                     int T, int D, float alpha, int window, int pattern,
                     float* dq, float* dk, float* dv, float* dalpha,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  BwdArgs a;
-  int st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
-                     pattern, workspace, workspace_bytes, &a);
+  bool empty = false;
+  int st = fsa::check_backward_call(q, k, v, dout, lse, dtype, B, H, T, D, alpha,
+                                    window, pattern, dq, dk, dv, dalpha, &empty);
   if (st != FSA_OK) return st;
-  if (dalpha == nullptr) return FSA_ERR_INVALID_ARG;
-  if (!a.empty && (!dq || !dk || !dv || !aligned16(dq) || !aligned16(dk) ||
-                   !aligned16(dv)))
-    return FSA_ERR_INVALID_ARG;
+  BwdArgs a;
+  st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window, pattern,
+                 workspace, workspace_bytes, &a);
+  if (st != FSA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.empty) return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
   st = hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
@@ -463,6 +483,8 @@ const char* fsa_status_string(int status) {
     case FSA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or size";
     case FSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FSA_ERR_HIP: return "HIP launch failed";
+    case FSA_ERR_SCRATCH:
+      return "problem needs more scratch than fsa_backward_noalloc's fixed device array";
     default: return "unknown status";
   }
 }

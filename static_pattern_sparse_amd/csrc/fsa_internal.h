@@ -36,6 +36,18 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype);
 
+// Argument checks of the backward entry points apart from the workspace:
+// pattern, shape, alpha, window, and the pointers (null, 16-byte alignment).
+// FSA_OK when the call may proceed; *empty is set for B*H*T == 0 (then only
+// dalpha is written).
+int check_backward_call(const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, int dtype, int B,
+                        int H, int T, int D, float alpha, int window,
+                        int pattern, const float* dq, const float* dk,
+                        const float* dv, const float* dalpha, bool* empty);
+// fsa_status of a HIP error (FSA_ERR_HIP, recorded for fsa_last_hip_error)
+int status_of(hipError_t e);
+
 // Launchers; each returns the hipError_t of its launch. The kernel family is
 // chosen from dtype: fp32 inputs use the lane-per-row kernels, bf16 inputs the
 // MFMA tile kernels. `out` is fp32, or bf16 (round to nearest even) when

@@ -18,6 +18,8 @@ FSA_ERR_INVALID_ARG = 1
 FSA_ERR_UNSUPPORTED = 2
 FSA_ERR_WORKSPACE = 3
 FSA_ERR_HIP = 4
+FSA_ERR_SCRATCH = 5
+FSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 FSA_SCHEDULE_FIXED = 0
 FSA_SCHEDULE_LINEAR = 1
@@ -44,7 +46,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsa.so")
 EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_offsets_ex", "fsa_forward",
            "fsa_forward_ex", "fsa_backward_workspace_size", "fsa_backward",
            "fsa_backward_ex", "fsa_backward_dq", "fsa_backward_dq_ex",
-           "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_decode",
+           "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_backward_noalloc",
+           "fsa_decode",
            "fsa_rope", "fsa_status_string", "fsa_last_hip_error")
 
 _lib = None
@@ -102,6 +105,9 @@ def lib():
         ex = getattr(L, name + "_ex")
         ex.argtypes = base[:12] + [i32] + base[12:]
         ex.restype = i32
+    L.fsa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                       f32, i32, i32, vp, vp, vp, vp, vp]
+    L.fsa_backward_noalloc.restype = i32
     L.fsa_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, i32,
                              i32, vp, vp, vp]
     L.fsa_decode.restype = i32
@@ -263,6 +269,28 @@ def fsa_backward(q, k, v, dout, lse, alpha, window, dq=None, dk=None, dv=None,
                             workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check("fsa_backward", st)
+    return dq, dk, dv, dalpha
+
+
+def fsa_backward_noalloc(q, k, v, dout, lse, alpha, window, dq, dk, dv, dalpha,
+                         stream=None, pattern=FSA_PATTERN_FIB):
+    """fsa_backward without a workspace: the library's fixed device scratch
+    serves instead, and nothing is allocated (dq, dk, dv [B,H,T,D] fp32 and
+    dalpha [1] fp32 are caller-supplied). Calls that overlap on one GPU race."""
+    import torch
+    B, H, T, D = _shape(q)
+    _rows(q, (k, v, dout))
+    f32 = torch.float32
+    _need(dq, (B, H, T, D), f32, "dq")
+    _need(dk, (B, H, T, D), f32, "dk")
+    _need(dv, (B, H, T, D), f32, "dv")
+    _need(lse, (B, H, T), f32, "lse")
+    _need(dalpha, (1,), f32, "dalpha")
+    st = lib().fsa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                    _dtype_code(q), B, H, T, D, float(alpha),
+                                    int(window), int(pattern), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(dalpha), _stream(stream))
+    _check("fsa_backward_noalloc", st)
     return dq, dk, dv, dalpha
 
 
