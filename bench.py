@@ -171,6 +171,45 @@ class Stack:
         for l in reversed(range(len(self.L))):
             self.order += [("bwd_dq",) + dq[l], ("bwd_dkdv",) + dkdv[l]]
 
+    def prepare_learned(self, torch, F, theta_map, optimizer, lr=1e-3):
+        """Launches of a learned-alpha step on the same buffers: every layer's
+        forward and backward read its tap table from device memory, and one
+        fsa_theta_step updates every layer's theta from the layers' dalpha
+        and writes the next step's alphas and tables. theta starts where
+        alpha = 1."""
+        import ctypes
+        lib = F.lib()
+        vp, f32 = ctypes.c_void_p, ctypes.c_float
+        wl, L = self.wl, self.layers
+        B, H, T, D = wl.B, wl.H, wl.T, wl.D
+        dt = F.FSA_DTYPE_BF16 if wl.dtype == "bf16" else F.FSA_DTYPE_F32
+        init = 1.0 if theta_map == F.FSA_THETA_CLAMP else 0.0
+        self.theta = torch.full((L,), init, dtype=torch.float32, device="cuda")
+        self.l_alpha = torch.empty(L, dtype=torch.float32, device="cuda")
+        self.l_tables = torch.empty((L, F.FSA_TAP_TABLE_BYTES), dtype=torch.uint8, device="cuda")
+        self.l_dalpha = torch.zeros(L, dtype=torch.float32, device="cuda")
+        self.l_state = torch.zeros(F.theta_state_bytes(L), dtype=torch.uint8, device="cuda")
+        F.fsa_theta_alpha(self.theta, theta_map, self.W, alpha=self.l_alpha, tables=self.l_tables)
+        stream = vp(torch.cuda.current_stream().cuda_stream)
+        fwd, bwd = [], []
+        for l, t in enumerate(self.L):
+            p = {n: vp(x.data_ptr()) for n, x in t.items()}
+            tab = vp(self.l_tables[l].data_ptr())
+            da = vp(self.l_dalpha[l:l + 1].data_ptr())
+            fwd.append(("fwd", lib.fsa_forward_dev, (p["q"], p["k"], p["v"], dt, B, H, T, D,
+                                                     tab, self.W, 0, p["out"], p["lse"],
+                                                     stream)))
+            bwd.append(("bwd", lib.fsa_backward_dev, (p["q"], p["k"], p["v"], p["dout"],
+                                                      p["lse"], dt, B, H, T, D, tab, self.W,
+                                                      p["dq"], p["dk"], p["dv"], da, p["ws"],
+                                                      t["ws"].numel(), stream)))
+        upd = ("theta_step", lib.fsa_theta_step,
+               (vp(self.theta.data_ptr()), vp(self.l_dalpha.data_ptr()), L, theta_map,
+                optimizer, f32(lr), f32(0.9), f32(0.999), f32(1e-8),
+                vp(self.l_state.data_ptr()), self.W, F.FSA_PATTERN_FIB,
+                vp(self.l_alpha.data_ptr()), vp(self.l_tables.data_ptr()), stream))
+        self.order = fwd + bwd[::-1] + [upd]
+
     def step(self, ev=None):
         for name, fn, args in self.order:
             if ev is not None:
@@ -658,6 +697,23 @@ def main():
         "kernels": kernels,
         "launches_per_step": counts,
     }
+    # the learned-alpha step on the same buffers (Adam on theta with the clip
+    # map): the layers' tables on the device, one update launch per step
+    stack.prepare_learned(torch, F, F.FSA_THETA_CLAMP, F.FSA_OPT_ADAM)
+    ms_l, per_l, _ = time_stack(stack, args.steps, args.warmup, torch)
+    alphas_now = stack.l_alpha.cpu().numpy()
+    res["learned"] = {
+        "workload": wl.name + " (learned alpha: clip map, Adam, theta from alpha = 1)",
+        "ms_per_step": round(ms_l, 4), "static_ms_per_step": round(ms_step, 4),
+        "ratio_to_static": round(ms_l / ms_step, 4),
+        "value": round(args.layers * wl.B * wl.H * wl.T / (ms_l * 1e-3), 1),
+        "median_us": {n: round(v * 1e3, 3) for n, v in per_l.items()},
+        "alpha_range_after": [round(float(alphas_now.min()), 6), round(float(alphas_now.max()), 6)]}
+    # back to the static schedule; one more static step refreshes the results
+    # that the oracle check reads
+    stack._prepare_calls(torch, F)
+    stack.step()
+    torch.cuda.synchronize()
     # the first and the last layer's GPU results, for the oracle check that
     # runs with the CPU baseline after every GPU leg
     snap1024 = stack.snapshot((0, args.layers - 1)) if not args.no_cpu_baseline else None

@@ -241,6 +241,94 @@ int fsa_backward_dkdv_ex(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * Learned alpha [DSFS: Methodology > Experimental variables, Learned: one free
+ * parameter theta per layer, initialised at alpha = 1 and trained by gradient
+ * descent; Architecture and attention > Scaling: alpha in [0.5, 1.5]; Core
+ * contributions and results > 2. Learned dilation is inert]. The page fixes
+ * neither the map from theta to alpha nor the optimizer; this library offers
+ *   FSA_THETA_CLAMP  alpha = clip(theta, 0.5, 1.5); after each update theta is
+ *                    projected back onto [0.5, 1.5] (projected gradient
+ *                    descent). theta = 1 gives alpha = 1.
+ *   FSA_THETA_TANH   alpha = 1 + tanh(theta)/2, theta unconstrained. theta = 0
+ *                    gives alpha = 1.
+ * alpha is the map evaluated in fp64 and rounded once to fp32. A layer's alpha
+ * and its tap table live in device memory, written by fsa_theta_alpha or
+ * fsa_theta_step; fsa_forward_dev and fsa_backward_dev read the table there,
+ * so a training step never brings alpha to the host.
+ */
+#define FSA_THETA_CLAMP 0
+#define FSA_THETA_TANH 1
+#define FSA_OPT_SGD 0  /* theta <- theta - lr * g */
+#define FSA_OPT_ADAM 1 /* Adam with bias correction (Kingma and Ba) */
+/* bytes of one layer's tap table (an opaque device record); tables of
+ * consecutive layers sit FSA_TAP_TABLE_BYTES apart from a 256-byte aligned base */
+#define FSA_TAP_TABLE_BYTES 256
+/* bytes of fsa_theta_step's optimizer state for L layers: m[L], v[L] (fp32)
+ * and the update count (int32) */
+#define FSA_THETA_STATE_BYTES(L) (8u * (unsigned)(L) + 16u)
+
+/*
+ * fsa_theta_alpha -- alpha and the tap table of every layer from its theta,
+ * on the device (one launch).
+ *   theta      device float[L], read; 1 <= L <= 1024.
+ *   theta_map  FSA_THETA_CLAMP or FSA_THETA_TANH.
+ *   window, pattern  the window and tap pattern (FSA_BASE_* | FSA_MODE_*) the
+ *             tables are for; the attention calls must pass the same window.
+ *   alpha      device float[L], written: the fp32 alpha of each layer (NaN
+ *             for a NaN theta; that layer's table then keeps no tap).
+ *   tap_tables device, L * FSA_TAP_TABLE_BYTES bytes, 256-byte aligned,
+ *             written: layer l's table at byte l * FSA_TAP_TABLE_BYTES.
+ * Returns FSA_ERR_INVALID_ARG for a bad L, map, window or pattern, or a null
+ * or misaligned pointer.
+ */
+int fsa_theta_alpha(const float* theta, int num_layers, int theta_map, int window,
+                    int pattern, float* alpha, void* tap_tables, void* stream);
+
+/*
+ * fsa_theta_step -- one optimizer update of every layer's theta from the
+ * layers' dL/dalpha, then the new alpha and tap tables, on the device (one
+ * launch, deterministic).
+ *   theta      device float[L], updated in place.
+ *   dalpha     device float[L]: dL/dalpha of each layer (fsa_backward_dev's
+ *             dalpha, one float per layer).
+ *   g_l = dalpha_l * dalpha/dtheta(theta_l): 1 on [0.5, 1.5] and 0 outside
+ *   for the clip, (1 - tanh(theta)^2)/2 for the tanh map. Then
+ *     FSA_OPT_SGD:  theta_l -= lr * g_l;
+ *     FSA_OPT_ADAM: t = count + 1; m = beta1 m + (1 - beta1) g,
+ *                   v = beta2 v + (1 - beta2) g^2,
+ *                   theta_l -= lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps);
+ *   with FSA_THETA_CLAMP theta is projected onto [0.5, 1.5]. The update is
+ *   computed in fp64; theta, m and v are stored in fp32.
+ *   state      device, FSA_THETA_STATE_BYTES(L) bytes, 16-byte aligned: m, v
+ *             and the update count, zero before the first update (the caller
+ *             clears it once); read and written.
+ *   lr >= 0 and finite; for Adam 0 <= beta1, beta2 < 1 and eps > 0.
+ *   window, pattern, alpha, tap_tables  as fsa_theta_alpha, for the new theta.
+ */
+int fsa_theta_step(float* theta, const float* dalpha, int num_layers, int theta_map,
+                   int optimizer, float lr, float beta1, float beta2, float eps,
+                   void* state, int window, int pattern, float* alpha,
+                   void* tap_tables, void* stream);
+
+/*
+ * fsa_forward_dev, fsa_backward_dev -- fsa_forward_ex and fsa_backward_ex with
+ * the layer's tap table read from device memory (one FSA_TAP_TABLE_BYTES
+ * record written by fsa_theta_alpha or fsa_theta_step, 16-byte aligned)
+ * instead of formed on the host from alpha. `window` must be the window the
+ * table was written for. fsa_forward_dev's `flags` is 0 or FSA_OUT_BF16.
+ * Arguments, layouts, results and errors otherwise as fsa_forward_ex and
+ * fsa_backward_ex; dalpha[0] is dL/dalpha of the layer.
+ */
+int fsa_forward_dev(const void* q, const void* k, const void* v, int dtype,
+                    int B, int H, int T, int D, const void* tap_table,
+                    int window, int flags, void* out, float* lse, void* stream);
+int fsa_backward_dev(const void* q, const void* k, const void* v,
+                     const void* dout, const float* lse, int dtype, int B, int H,
+                     int T, int D, const void* tap_table, int window, float* dq,
+                     float* dk, float* dv, float* dalpha, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * fsa_backward_noalloc -- fsa_backward_ex with no workspace argument and no
  * allocation, for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.

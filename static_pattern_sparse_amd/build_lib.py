@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfsa.so")
 SOURCES = ["fsa_api.cpp", "fsa_vec.hip", "fsa_mfma.hip", "fsa_decode.hip", "fsa_rope.hip",
-           "fsa_noalloc.hip"]
+           "fsa_learned.hip", "fsa_noalloc.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -9,68 +9,15 @@
 
 #include "fsa.h"
 #include "fsa_internal.h"
+#include "fsa_taps.h"
 
 namespace fsa {
 
 namespace {
 
-// Methodology > Architecture and attention > Attended set: Fibonacci distances
-// 1 .. 987 with the leading 1 taken once.
-constexpr int kFib[kNumTaps] = {1,  2,  3,   5,   8,   13,  21, 34,
-                                55, 89, 144, 233, 377, 610, 987};
-
-// Methodology > Control variables: the power-of-two (log-sparse) control base.
-// Fifteen terms 1, 2, 4, ..., 16384, as many as the Fibonacci list. The page's
-// examples of offsets that only a longer evaluation reaches (1024 and 2048 at
-// four times a 1024 training length, Results > Length extrapolation, base
-// sensitivity) need a ladder that goes on past 987; terms beyond a sequence's
-// length attend nothing.
-constexpr int kNumPow2 = 15;
-constexpr int kPow2[kNumPow2] = {1,   2,   4,    8,    16,   32,   64,  128,
-                                 256, 512, 1024, 2048, 4096, 8192, 16384};
-
-// Base distances of a pattern: the list and its length.
-const int* base_list(int pattern, int* n) {
-  if ((pattern & FSA_BASE_MASK) == FSA_BASE_POW2) {
-    *n = kNumPow2;
-    return kPow2;
-  }
-  *n = kNumTaps;
-  return kFib;
-}
-
 bool pattern_ok(int pattern) {
   return (pattern & ~(FSA_BASE_MASK | FSA_MODE_MASK | FSA_OUT_BF16)) == 0 &&
          (pattern & FSA_BASE_MASK) <= FSA_BASE_POW2;
-}
-
-// Nearest integer to d >= 0, ties to the even neighbour.
-double round_even(double d) {
-  const double f = std::floor(d);
-  const double r = d - f;
-  if (r > 0.5) return f + 1.0;
-  if (r < 0.5) return f;
-  return std::fmod(f, 2.0) == 0.0 ? f : f + 1.0;
-}
-
-// One base distance at scale alpha: the distance c of the lower row, the
-// weight t of the upper row and the slope d(position)/d(alpha). The distance
-// alpha*f is exact in fp64 (24 + 15 significant bits).
-//   interpolated (Methodology > Architecture and attention > Implementation):
-//     c = ceil(d), t = c - d, slope -f;
-//   rounded (the integer offsets that let static runs take a fused mask path,
-//   Core contributions and results > 2. Learned dilation is inert, efficiency):
-//     c = round(d), t = 0, slope 0 -- the attended rows do not move with alpha.
-void tap_of(int pattern, double d, double f, double* c, double* t, double* slope) {
-  if (pattern & FSA_MODE_ROUND) {
-    *c = round_even(d);
-    *t = 0.0;
-    *slope = 0.0;
-  } else {
-    *c = std::ceil(d);
-    *t = *c - d;
-    *slope = -f;
-  }
 }
 
 thread_local int g_last_hip_error = 0;
@@ -84,25 +31,6 @@ int gcd(int a, int b) {
     b = t;
   }
   return a < 0 ? -a : a;
-}
-
-// Tap table of one layer: the kept base distances (alpha*f >= W), ascending.
-// Each weight is rounded once to fp32 from its exact fp64 value.
-void build_taps(int pattern, float alpha, int window, Taps* t) {
-  int nb = 0;
-  const int* f = base_list(pattern, &nb);
-  *t = Taps{};                                        // unused slots zero
-  for (int k = 0; k < nb; ++k) {
-    const double d = static_cast<double>(alpha) * f[k];
-    if (d < static_cast<double>(window)) continue;   // inside the window
-    double c, hi, slope;
-    tap_of(pattern, d, f[k], &c, &hi, &slope);
-    const int n = t->n++;
-    t->c[n] = static_cast<int>(c);
-    t->w_hi[n] = static_cast<float>(hi);
-    t->w_lo[n] = static_cast<float>(1.0 - hi);
-    t->neg_f[n] = static_cast<float>(slope);
-  }
 }
 
 bool aligned16(const void* p) {
@@ -141,18 +69,24 @@ int hip_status(hipError_t e) {
 struct BwdArgs {
   bool empty = false;
   Problem pr{};
-  Taps taps{};
+  TapsArg taps{};
   float* delta = nullptr;
   float* partials = nullptr;
 };
 
 BwdWorkspace bwd_layout(int B, int H, int T, int D, int dtype);
 
-// Checks shared by the backward stages; fills *a on success.
+// Checks shared by the backward stages; fills *a on success. The tap table
+// comes from alpha and the pattern, or from `table` (device memory) when that
+// is not null; alpha and the pattern are then not used.
 int check_bwd(const void* q, const void* k, const void* v, const void* dout,
               const float* lse, int dtype, int B, int H, int T, int D,
               float alpha, int window, int pattern, void* workspace,
-              size_t workspace_bytes, BwdArgs* a) {
+              size_t workspace_bytes, BwdArgs* a, const Taps* table = nullptr) {
+  if (table != nullptr) {
+    alpha = 1.0f;
+    pattern = FSA_PATTERN_FIB;
+  }
   if (!pattern_ok(pattern)) return FSA_ERR_INVALID_ARG;
   int st = check_shape(dtype, B, H, T, D, alpha, window);
   if (st != FSA_OK) return st;
@@ -166,7 +100,13 @@ int check_bwd(const void* q, const void* k, const void* v, const void* dout,
   if (workspace == nullptr || workspace_bytes < ws.total ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FSA_ERR_WORKSPACE;
-  build_taps(pattern, alpha, window, &a->taps);
+  if (table != nullptr) {
+    a->taps.v = Taps{};
+    a->taps.dev = table;
+  } else {
+    build_taps(pattern, alpha, window, &a->taps.v);
+    a->taps.dev = nullptr;
+  }
   a->pr = make_problem(B, H, T, D, window);
   char* wsb = static_cast<char*>(workspace);
   a->delta = reinterpret_cast<float*>(wsb + ws.delta_off);
@@ -198,7 +138,7 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
 // Kernel family: bf16 inputs take the MFMA tile kernels, fp32 inputs the
 // lane-per-row kernels.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
-                          int dtype, const Problem& pr, const Taps& taps,
+                          int dtype, const Problem& pr, const TapsArg& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s) {
   if (mfma_supported(pr, dtype))
     return launch_fwd_mfma(q, k, v, pr, taps, out, out_bf16, lse, s);
@@ -207,7 +147,7 @@ hipError_t launch_forward(const void* q, const void* k, const void* v,
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, int dtype,
-                         const Problem& pr, const Taps& taps, float* dq,
+                         const Problem& pr, const TapsArg& taps, float* dq,
                          float* delta, float* partials, hipStream_t s) {
   if (mfma_supported(pr, dtype))
     return launch_bwd_dq_mfma(q, k, v, dout, lse, pr, taps, dq, delta, partials, s);
@@ -218,7 +158,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
                            const void* dout, const float* lse,
                            const float* delta, const float* partials,
-                           int dtype, const Problem& pr, const Taps& taps,
+                           int dtype, const Problem& pr, const TapsArg& taps,
                            float* dk, float* dv, float* dalpha, hipStream_t s) {
   const size_t np = bwd_partials_used(pr, dtype);
   if (mfma_supported(pr, dtype))
@@ -254,6 +194,30 @@ int check_backward_call(const void* q, const void* k, const void* v,
 }
 
 int status_of(hipError_t e) { return hip_status(e); }
+
+int backward_both(const void* q, const void* k, const void* v, const void* dout,
+                  const float* lse, int dtype, int B, int H, int T, int D,
+                  float alpha, int window, int pattern, const Taps* table,
+                  float* dq, float* dk, float* dv, float* dalpha, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int st = check_backward_call(q, k, v, dout, lse, dtype, B, H, T, D,
+                               table ? 1.0f : alpha, window,
+                               table ? FSA_PATTERN_FIB : pattern, dq, dk, dv,
+                               dalpha, &empty);
+  if (st != FSA_OK) return st;
+  BwdArgs a;
+  st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window, pattern,
+                 workspace, workspace_bytes, &a, table);
+  if (st != FSA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.empty) return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
+  st = hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
+                                a.delta, a.partials, s));
+  if (st != FSA_OK) return st;
+  return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, a.partials,
+                                    dtype, a.pr, a.taps, dk, dv, dalpha, s));
+}
 
 }  // namespace fsa
 
@@ -296,12 +260,11 @@ int fsa_offsets_ex(int pattern, float alpha, int window, int32_t* c_out,
   if (!c_out || !t_out || !keep_out || window < 1 || !alpha_ok(alpha) ||
       !pattern_ok(pattern))
     return FSA_ERR_INVALID_ARG;
-  int nb = 0;
-  const int* f = base_list(pattern, &nb);
-  for (int k = 0; k < nb; ++k) {
-    const double d = static_cast<double>(alpha) * f[k];
+  for (int k = 0; k < kNumTaps; ++k) {
+    const double f = base_term(pattern, k);
+    const double d = static_cast<double>(alpha) * f;
     double c, t, slope;
-    tap_of(pattern, d, f[k], &c, &t, &slope);
+    tap_of(pattern, d, f, &c, &t, &slope);
     c_out[k] = static_cast<int32_t>(c);
     t_out[k] = static_cast<float>(t);
     keep_out[k] = d >= static_cast<double>(window) ? 1 : 0;
@@ -325,8 +288,8 @@ int fsa_forward_ex(const void* q, const void* k, const void* v, int dtype,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       !aligned16(lse))
     return FSA_ERR_INVALID_ARG;
-  Taps taps;
-  build_taps(pattern, alpha, window, &taps);
+  TapsArg taps{};
+  build_taps(pattern, alpha, window, &taps.v);
   const Problem pr = make_problem(B, H, T, D, window);
   return hip_status(launch_forward(q, k, v, dtype, pr, taps, out,
                                    (pattern & FSA_OUT_BF16) != 0, lse,
@@ -384,21 +347,39 @@ int fsa_backward_ex(const void* q, const void* k, const void* v,
                     int T, int D, float alpha, int window, int pattern,
                     float* dq, float* dk, float* dv, float* dalpha,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  bool empty = false;
-  int st = fsa::check_backward_call(q, k, v, dout, lse, dtype, B, H, T, D, alpha,
-                                    window, pattern, dq, dk, dv, dalpha, &empty);
+  return fsa::backward_both(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window,
+                            pattern, nullptr, dq, dk, dv, dalpha, workspace,
+                            workspace_bytes, stream);
+}
+
+int fsa_forward_dev(const void* q, const void* k, const void* v, int dtype,
+                    int B, int H, int T, int D, const void* tap_table,
+                    int window, int flags, void* out, float* lse, void* stream) {
+  if ((flags & ~FSA_OUT_BF16) != 0) return FSA_ERR_INVALID_ARG;
+  int st = check_shape(dtype, B, H, T, D, 1.0f, window);
   if (st != FSA_OK) return st;
-  BwdArgs a;
-  st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window, pattern,
-                 workspace, workspace_bytes, &a);
-  if (st != FSA_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.empty) return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
-  st = hip_status(launch_bwd_dq(q, k, v, dout, lse, dtype, a.pr, a.taps, dq,
-                                a.delta, a.partials, s));
-  if (st != FSA_OK) return st;
-  return hip_status(launch_bwd_dkdv(q, k, v, dout, lse, a.delta, a.partials,
-                                    dtype, a.pr, a.taps, dk, dv, dalpha, s));
+  if (static_cast<long long>(B) * H * T == 0) return FSA_OK;
+  if (!q || !k || !v || !out || !lse || !tap_table) return FSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(tap_table))
+    return FSA_ERR_INVALID_ARG;
+  TapsArg taps{};
+  taps.dev = static_cast<const Taps*>(tap_table);
+  const Problem pr = make_problem(B, H, T, D, window);
+  return hip_status(launch_forward(q, k, v, dtype, pr, taps, out,
+                                   (flags & FSA_OUT_BF16) != 0, lse,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int fsa_backward_dev(const void* q, const void* k, const void* v,
+                     const void* dout, const float* lse, int dtype, int B, int H,
+                     int T, int D, const void* tap_table, int window, float* dq,
+                     float* dk, float* dv, float* dalpha, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (tap_table == nullptr || !aligned16(tap_table)) return FSA_ERR_INVALID_ARG;
+  return fsa::backward_both(q, k, v, dout, lse, dtype, B, H, T, D, 1.0f, window,
+                            FSA_PATTERN_FIB, static_cast<const Taps*>(tap_table),
+                            dq, dk, dv, dalpha, workspace, workspace_bytes, stream);
 }
 
 int fsa_backward_dq(const void* q, const void* k, const void* v,
@@ -444,8 +425,8 @@ int fsa_decode(const void* q, const void* k_cache, const void* v_cache,
       !aligned16(out) || (reinterpret_cast<uintptr_t>(pos) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return FSA_ERR_INVALID_ARG;
-  Taps taps;
-  build_taps(pattern, alpha, window, &taps);
+  TapsArg taps{};
+  build_taps(pattern, alpha, window, &taps.v);
   return hip_status(launch_decode(q, k_cache, v_cache, dtype, pos, B, H, T_cap,
                                   D, window, taps, out,
                                   (pattern & FSA_OUT_BF16) != 0, lse,

@@ -84,7 +84,7 @@ __device__ __forceinline__ void write_lane(int* x, int v) {
 }
 
 template <int L>
-__device__ __forceinline__ void fill_lanes(const Taps& taps, int* c, int* wl, int* wh) {
+__device__ __forceinline__ void fill_lanes(CTaps& taps, int* c, int* wl, int* wh) {
   if constexpr (L < kNumTaps) {
     write_lane<L>(c, taps.c[L]);
     write_lane<L>(wl, __float_as_int(taps.w_lo[L]));
@@ -93,7 +93,7 @@ __device__ __forceinline__ void fill_lanes(const Taps& taps, int* c, int* wl, in
   }
 }
 
-__device__ __forceinline__ TapLanes tap_lanes(const Taps& taps) {
+__device__ __forceinline__ TapLanes tap_lanes(CTaps& taps) {
   int c = taps.c[0], wl = __float_as_int(taps.w_lo[0]), wh = __float_as_int(taps.w_hi[0]);
   fill_lanes<1>(taps, &c, &wl, &wh);
   return TapLanes{c, __int_as_float(wl), __int_as_float(wh)};
@@ -146,7 +146,8 @@ template <typename Tin, int D, typename OutT>
 __global__ __launch_bounds__(kDecBlock) void decode_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ kc,
     const Tin* __restrict__ vc, const int* __restrict__ pos, int H, int Tcap,
-    int W, float c2, Taps taps, OutT* __restrict__ out, float* __restrict__ lse) {
+    int W, float c2, TapsArg taps_arg, OutT* __restrict__ out, float* __restrict__ lse) {
+  CTaps& taps = taps_of(taps_arg);
   constexpr int C = D / 16;
   constexpr float kLn2 = 0.6931471805599453f;
   __shared__ float s_m[kGroups], s_l[kGroups];
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kDecBlock) void decode_kernel(
 template <typename Tin, int D>
 hipError_t decode_typed(const void* q, const void* k, const void* v,
                         const int* pos, int B, int H, int Tcap, int W,
-                        const Taps& taps, void* out, bool out_bf16, float* lse,
+                        const TapsArg& taps, void* out, bool out_bf16, float* lse,
                         hipStream_t s) {
   const float c2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
   if (out_bf16)
@@ -274,7 +275,7 @@ hipError_t decode_typed(const void* q, const void* k, const void* v,
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype,
                          const int* pos, int B, int H, int Tcap, int D, int W,
-                         const Taps& taps, void* out, bool out_bf16, float* lse,
+                         const TapsArg& taps, void* out, bool out_bf16, float* lse,
                          hipStream_t s) {
   if (dtype == FSA_DTYPE_F32)
     return D == 64 ? decode_typed<float, 64>(q, k, v, pos, B, H, Tcap, W, taps, out, out_bf16, lse, s)

@@ -21,6 +21,22 @@ struct Taps {
   float neg_f[kNumTaps];   // -f_k, d(position)/d(alpha) of the tap
 };
 
+// A layer's tap table as the kernels receive it: by value from the host
+// planner, or, when `dev` is not null, from device memory -- a table written
+// on the device from a device-resident alpha (fsa_theta_alpha,
+// fsa_theta_step), so that a learned alpha never travels to the host.
+struct TapsArg {
+  Taps v;
+  const Taps* dev;
+};
+
+// The table a kernel reads, in the constant address space: the kernel's own
+// argument copy or the device table, both read with scalar loads.
+typedef __attribute__((address_space(4))) const Taps CTaps;
+__device__ __forceinline__ CTaps& taps_of(const TapsArg& a) {
+  return a.dev ? *(CTaps*)a.dev : *(CTaps*)&a.v;
+}
+
 struct Problem {
   int B, H, T, D, W;
   float scale;  // 1/sqrt(D)
@@ -47,23 +63,31 @@ int check_backward_call(const void* q, const void* k, const void* v,
                         const float* dv, const float* dalpha, bool* empty);
 // fsa_status of a HIP error (FSA_ERR_HIP, recorded for fsa_last_hip_error)
 int status_of(hipError_t e);
+// The whole backward (dq stage, then dk/dv stage) after every check; the tap
+// table from (alpha, pattern), or from `table` in device memory when that is
+// not null.
+int backward_both(const void* q, const void* k, const void* v, const void* dout,
+                  const float* lse, int dtype, int B, int H, int T, int D,
+                  float alpha, int window, int pattern, const Taps* table,
+                  float* dq, float* dk, float* dv, float* dalpha, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 // Launchers; each returns the hipError_t of its launch. The kernel family is
 // chosen from dtype: fp32 inputs use the lane-per-row kernels, bf16 inputs the
 // MFMA tile kernels. `out` is fp32, or bf16 (round to nearest even) when
 // out_bf16.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
-                          int dtype, const Problem& pr, const Taps& taps,
+                          int dtype, const Problem& pr, const TapsArg& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v,
                          const void* dout, const float* lse, int dtype,
-                         const Problem& pr, const Taps& taps, float* dq,
+                         const Problem& pr, const TapsArg& taps, float* dq,
                          float* delta, float* partials, hipStream_t s);
 // dk, dv, and dalpha[0] = fixed-order sum of the dq stage's partials
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v,
                            const void* dout, const float* lse,
                            const float* delta, const float* partials,
-                           int dtype, const Problem& pr, const Taps& taps,
+                           int dtype, const Problem& pr, const TapsArg& taps,
                            float* dk, float* dv, float* dalpha, hipStream_t s);
 // number of dalpha partials the dq stage writes for this problem
 size_t bwd_partials_used(const Problem& pr, int dtype);
@@ -74,7 +98,7 @@ hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
 // against rows 0..pos[b] of the cached slabs [B][H][Tcap][D]
 hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype,
                          const int* pos, int B, int H, int Tcap, int D, int W,
-                         const Taps& taps, void* out, bool out_bf16, float* lse,
+                         const TapsArg& taps, void* out, bool out_bf16, float* lse,
                          hipStream_t s);
 
 // rotary position embedding pass (fsa_rope.hip): rows [B][H][T][D] of
@@ -88,33 +112,33 @@ long long rope_blocks(int B, int H, int T, int D);
 
 // lane-per-row kernels (fsa_vec.hip)
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
-                          int dtype, const Problem& pr, const Taps& taps,
+                          int dtype, const Problem& pr, const TapsArg& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s);
 hipError_t launch_bwd_dq_vec(const void* q, const void* k, const void* v,
                              const void* dout, const float* lse, int dtype,
-                             const Problem& pr, const Taps& taps, float* dq,
+                             const Problem& pr, const TapsArg& taps, float* dq,
                              float* delta, float* partials, hipStream_t s);
 hipError_t launch_bwd_dkdv_vec(const void* q, const void* k, const void* v,
                                const void* dout, const float* lse,
                                const float* delta, int dtype,
-                               const Problem& pr, const Taps& taps, float* dk,
+                               const Problem& pr, const TapsArg& taps, float* dk,
                                float* dv, hipStream_t s);
 size_t bwd_partials_used_vec(const Problem& pr);
 
 // MFMA tile kernels (fsa_mfma.hip): bf16 inputs, D in {64, 128}, any window
 bool mfma_supported(const Problem& pr, int dtype);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
-                           const Problem& pr, const Taps& taps, void* out,
+                           const Problem& pr, const TapsArg& taps, void* out,
                            bool out_bf16, float* lse, hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               const void* dout, const float* lse,
-                              const Problem& pr, const Taps& taps, float* dq,
+                              const Problem& pr, const TapsArg& taps, float* dq,
                               float* delta, float* partials, hipStream_t s);
 hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse,
                                 const float* delta, const float* partials,
                                 size_t n_partials, const Problem& pr,
-                                const Taps& taps, float* dk, float* dv,
+                                const TapsArg& taps, float* dk, float* dv,
                                 float* dalpha, hipStream_t s);
 size_t bwd_partials_used_mfma(const Problem& pr);
 

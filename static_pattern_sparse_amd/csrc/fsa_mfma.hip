@@ -406,7 +406,7 @@ __device__ __forceinline__ void write_lane(int* x, int v) {
 }
 
 template <int L>
-__device__ __forceinline__ void fill_tap_lanes(const Taps& taps, int* c, int* wl, int* wh, int* nf) {
+__device__ __forceinline__ void fill_tap_lanes(CTaps& taps, int* c, int* wl, int* wh, int* nf) {
   if constexpr (L < kNumTaps) {
     write_lane<L>(c, taps.c[L]);
     write_lane<L>(wl, __float_as_int(taps.w_lo[L]));
@@ -418,7 +418,7 @@ __device__ __forceinline__ void fill_tap_lanes(const Taps& taps, int* c, int* wl
 
 // Built with v_writelane (one per tap and field), so that the compiler does
 // not turn a per-lane select into an indexed copy of the argument block.
-__device__ __forceinline__ TapLane tap_lane(const Taps& taps) {
+__device__ __forceinline__ TapLane tap_lane(CTaps& taps) {
   int c = taps.c[0], wl = __float_as_int(taps.w_lo[0]);
   int wh = __float_as_int(taps.w_hi[0]), nf = __float_as_int(taps.neg_f[0]);
   fill_tap_lanes<1>(taps, &c, &wl, &wh, &nf);
@@ -577,8 +577,9 @@ __device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, uint
 template <int D, typename OutT>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, Problem pr, Taps taps, int n_tiles, int hg,
+    const uint16_t* __restrict__ v, Problem pr, TapsArg taps_arg, int n_tiles, int hg,
     OutT* __restrict__ out, float* __restrict__ lse) {
+  CTaps& taps = taps_of(taps_arg);
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;         // K_x K_y V_x V_y
   constexpr float kLog2e = 1.4426950408889634f;
@@ -747,9 +748,10 @@ template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, Problem pr, Taps taps, int n_tiles, int hg,
+    const float* __restrict__ lse, Problem pr, TapsArg taps_arg, int n_tiles, int hg,
     float* __restrict__ dq, float* __restrict__ delta,
     float* __restrict__ partials) {
+  CTaps& taps = taps_of(taps_arg);
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // K_x K_y V_x V_y
   constexpr float kLog2e = 1.4426950408889634f;
@@ -953,9 +955,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
-    const float* __restrict__ partials, int n_partials, Problem pr, Taps taps,
+    const float* __restrict__ partials, int n_partials, Problem pr, TapsArg taps_arg,
     int n_tiles, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dalpha) {
+  CTaps& taps = taps_of(taps_arg);
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // Q_x Q_y G_x G_y
   __shared__ __attribute__((aligned(16))) char smem[kStage];
@@ -1185,7 +1188,7 @@ static int head_group(const Problem& pr, int cap) {
 }
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
-                           const Problem& pr, const Taps& taps, void* out,
+                           const Problem& pr, const TapsArg& taps, void* out,
                            bool out_bf16, float* lse, hipStream_t s) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
@@ -1223,7 +1226,7 @@ size_t bwd_partials_used_mfma(const Problem& pr) {
 
 hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               const void* dout, const float* lse,
-                              const Problem& pr, const Taps& taps, float* dq,
+                              const Problem& pr, const TapsArg& taps, float* dq,
                               float* delta, float* partials, hipStream_t s) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
@@ -1245,7 +1248,7 @@ hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse,
                                 const float* delta, const float* partials,
                                 size_t n_partials, const Problem& pr,
-                                const Taps& taps, float* dk, float* dv,
+                                const TapsArg& taps, float* dk, float* dv,
                                 float* dalpha, hipStream_t s) {
   const int n_tiles = (pr.T + kTileK - 1) / kTileK;
   const dim3 grid(n_tiles * pr.B * pr.H);

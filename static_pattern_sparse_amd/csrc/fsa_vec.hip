@@ -101,8 +101,9 @@ __device__ __forceinline__ void axpy_row(float a, const Tin* p, float* acc) {
 template <typename Tin, int D, typename OutT>
 __global__ __launch_bounds__(kVecBlock) void fwd_vec_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k,
-    const Tin* __restrict__ v, Problem pr, Taps taps, OutT* __restrict__ out,
+    const Tin* __restrict__ v, Problem pr, TapsArg taps_arg, OutT* __restrict__ out,
     float* __restrict__ lse) {
+  CTaps& taps = taps_of(taps_arg);
   const int i = blockIdx.x * kVecBlock + threadIdx.x;
   const int T = pr.T;
   if (i >= T) return;
@@ -165,9 +166,10 @@ template <typename Tin, int D>
 __global__ __launch_bounds__(kVecBlock) void bwd_dq_vec_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ dout,
-    const float* __restrict__ lse, Problem pr, Taps taps,
+    const float* __restrict__ lse, Problem pr, TapsArg taps_arg,
     float* __restrict__ dq, float* __restrict__ delta,
     float* __restrict__ partials) {
+  CTaps& taps = taps_of(taps_arg);
   const int i = blockIdx.x * kVecBlock + threadIdx.x;
   const int T = pr.T;
   float dal = 0.f;
@@ -247,7 +249,8 @@ __global__ __launch_bounds__(kVecBlock) void bwd_dkdv_vec_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, Problem pr,
-    Taps taps, float* __restrict__ dk, float* __restrict__ dv) {
+    TapsArg taps_arg, float* __restrict__ dk, float* __restrict__ dv) {
+  CTaps& taps = taps_of(taps_arg);
   const int j = blockIdx.x * kVecBlock + threadIdx.x;
   const int T = pr.T;
   if (j >= T) return;
@@ -354,7 +357,7 @@ hipError_t launch_dalpha_reduce(const float* partials, size_t n, float* dalpha,
 namespace {
 template <typename Tin, int D>
 hipError_t fwd_vec_typed(const void* q, const void* k, const void* v,
-                         const Problem& pr, const Taps& taps, void* out,
+                         const Problem& pr, const TapsArg& taps, void* out,
                          bool out_bf16, float* lse, hipStream_t s) {
   dim3 grid((pr.T + kVecBlock - 1) / kVecBlock, pr.B * pr.H);
   if (out_bf16)
@@ -371,7 +374,7 @@ hipError_t fwd_vec_typed(const void* q, const void* k, const void* v,
 template <typename Tin, int D>
 hipError_t bwd_dq_vec_typed(const void* q, const void* k, const void* v,
                             const void* dout, const float* lse,
-                            const Problem& pr, const Taps& taps, float* dq,
+                            const Problem& pr, const TapsArg& taps, float* dq,
                             float* delta, float* partials, hipStream_t s) {
   dim3 grid((pr.T + kVecBlock - 1) / kVecBlock, pr.B * pr.H);
   hipLaunchKernelGGL((bwd_dq_vec_kernel<Tin, D>), grid, dim3(kVecBlock), 0, s,
@@ -385,7 +388,7 @@ template <typename Tin, int D>
 hipError_t bwd_dkdv_vec_typed(const void* q, const void* k, const void* v,
                               const void* dout, const float* lse,
                               const float* delta, const Problem& pr,
-                              const Taps& taps, float* dk, float* dv,
+                              const TapsArg& taps, float* dk, float* dv,
                               hipStream_t s) {
   dim3 grid((pr.T + kVecBlock - 1) / kVecBlock, pr.B * pr.H);
   hipLaunchKernelGGL((bwd_dkdv_vec_kernel<Tin, D>), grid, dim3(kVecBlock), 0, s,
@@ -397,7 +400,7 @@ hipError_t bwd_dkdv_vec_typed(const void* q, const void* k, const void* v,
 }  // namespace
 
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
-                          int dtype, const Problem& pr, const Taps& taps,
+                          int dtype, const Problem& pr, const TapsArg& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s) {
   if (dtype == FSA_DTYPE_F32) {
     return pr.D == 64 ? fwd_vec_typed<float, 64>(q, k, v, pr, taps, out, out_bf16, lse, s)
@@ -413,7 +416,7 @@ size_t bwd_partials_used_vec(const Problem& pr) {
 
 hipError_t launch_bwd_dq_vec(const void* q, const void* k, const void* v,
                              const void* dout, const float* lse, int dtype,
-                             const Problem& pr, const Taps& taps, float* dq,
+                             const Problem& pr, const TapsArg& taps, float* dq,
                              float* delta, float* partials, hipStream_t s) {
   if (dtype == FSA_DTYPE_F32)
     return pr.D == 64 ? bwd_dq_vec_typed<float, 64>(q, k, v, dout, lse, pr, taps, dq, delta, partials, s)
@@ -425,7 +428,7 @@ hipError_t launch_bwd_dq_vec(const void* q, const void* k, const void* v,
 hipError_t launch_bwd_dkdv_vec(const void* q, const void* k, const void* v,
                                const void* dout, const float* lse,
                                const float* delta, int dtype,
-                               const Problem& pr, const Taps& taps, float* dk,
+                               const Problem& pr, const TapsArg& taps, float* dk,
                                float* dv, hipStream_t s) {
   if (dtype == FSA_DTYPE_F32)
     return pr.D == 64 ? bwd_dkdv_vec_typed<float, 64>(q, k, v, dout, lse, delta, pr, taps, dk, dv, s)

@@ -37,6 +37,19 @@ FSA_MODE_LERP = 0
 FSA_MODE_ROUND = 2
 FSA_PATTERN_FIB = FSA_BASE_FIBONACCI | FSA_MODE_LERP
 FSA_OUT_BF16 = 4
+# learned alpha: theta -> alpha maps, optimizers, device record sizes
+FSA_THETA_CLAMP = 0
+FSA_THETA_TANH = 1
+FSA_OPT_SGD = 0
+FSA_OPT_ADAM = 1
+FSA_TAP_TABLE_BYTES = 256
+
+
+def theta_state_bytes(num_layers):
+    """FSA_THETA_STATE_BYTES(L): m[L], v[L] and the update count."""
+    return 8 * int(num_layers) + 16
+
+
 PATTERNS = {"fib": FSA_PATTERN_FIB,
             "fib-round": FSA_BASE_FIBONACCI | FSA_MODE_ROUND,
             "pow2": FSA_BASE_POW2 | FSA_MODE_LERP,
@@ -47,7 +60,8 @@ EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_offsets_ex", "fsa_forward",
            "fsa_forward_ex", "fsa_backward_workspace_size", "fsa_backward",
            "fsa_backward_ex", "fsa_backward_dq", "fsa_backward_dq_ex",
            "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_backward_noalloc",
-           "fsa_decode",
+           "fsa_decode", "fsa_theta_alpha", "fsa_theta_step", "fsa_forward_dev",
+           "fsa_backward_dev",
            "fsa_rope", "fsa_status_string", "fsa_last_hip_error")
 
 _lib = None
@@ -108,6 +122,17 @@ def lib():
     L.fsa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                        f32, i32, i32, vp, vp, vp, vp, vp]
     L.fsa_backward_noalloc.restype = i32
+    L.fsa_theta_alpha.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    L.fsa_theta_alpha.restype = i32
+    L.fsa_theta_step.argtypes = [vp, vp, i32, i32, i32, f32, f32, f32, f32, vp, i32,
+                                 i32, vp, vp, vp]
+    L.fsa_theta_step.restype = i32
+    L.fsa_forward_dev.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32,
+                                  vp, vp, vp]
+    L.fsa_forward_dev.restype = i32
+    L.fsa_backward_dev.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
+                                   i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.fsa_backward_dev.restype = i32
     L.fsa_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, i32,
                              i32, vp, vp, vp]
     L.fsa_decode.restype = i32
@@ -385,3 +410,99 @@ def fsa_rope(x, base, pos0=None, inverse=False, out=None, out_dtype=None,
                         _dtype_code(out), _stream(stream))
     _check("fsa_rope", st)
     return out
+
+
+# ------------------------------------------------------------- learned alpha
+def _f32_dev(t, n, name):
+    import torch
+    return _need(t, (n,), torch.float32, name)
+
+
+def fsa_theta_alpha(theta, theta_map, window, pattern=FSA_PATTERN_FIB, alpha=None,
+                    tables=None, stream=None):
+    """alpha [L] fp32 and the layers' tap tables (uint8 [L, 256] device
+    records) from theta [L] fp32, on the device."""
+    import torch
+    if not isinstance(theta, torch.Tensor) or theta.dim() != 1:
+        raise ValueError("theta must be a 1-D device tensor")
+    L = int(theta.shape[0])
+    _f32_dev(theta, L, "theta")
+    if alpha is None:
+        alpha = torch.empty(L, dtype=torch.float32, device=theta.device)
+    if tables is None:
+        tables = torch.empty((L, FSA_TAP_TABLE_BYTES), dtype=torch.uint8, device=theta.device)
+    _f32_dev(alpha, L, "alpha")
+    _need(tables, (L, FSA_TAP_TABLE_BYTES), torch.uint8, "tables")
+    st = lib().fsa_theta_alpha(_ptr(theta), L, int(theta_map), int(window), int(pattern),
+                               _ptr(alpha), _ptr(tables), _stream(stream))
+    _check("fsa_theta_alpha", st)
+    return alpha, tables
+
+
+def fsa_theta_step(theta, dalpha, theta_map, optimizer, lr, state, alpha, tables,
+                   window, pattern=FSA_PATTERN_FIB, beta1=0.9, beta2=0.999, eps=1e-8,
+                   stream=None):
+    """One optimizer update of theta [L] from dalpha [L] (device fp32); state is
+    a zeroed uint8 device tensor of theta_state_bytes(L) at the first update;
+    alpha and tables receive the new alpha and tap tables."""
+    import torch
+    L = int(theta.shape[0])
+    _f32_dev(theta, L, "theta")
+    _f32_dev(dalpha, L, "dalpha")
+    _f32_dev(alpha, L, "alpha")
+    _need(tables, (L, FSA_TAP_TABLE_BYTES), torch.uint8, "tables")
+    _need(state, (theta_state_bytes(L),), torch.uint8, "state")
+    st = lib().fsa_theta_step(_ptr(theta), _ptr(dalpha), L, int(theta_map), int(optimizer),
+                              float(lr), float(beta1), float(beta2), float(eps),
+                              _ptr(state), int(window), int(pattern), _ptr(alpha),
+                              _ptr(tables), _stream(stream))
+    _check("fsa_theta_step", st)
+
+
+def fsa_forward_dev(q, k, v, table, window, out=None, lse=None, stream=None,
+                    out_dtype=None):
+    """fsa_forward with the layer's tap table from device memory (a row of the
+    tables that fsa_theta_alpha / fsa_theta_step write)."""
+    import torch
+    B, H, T, D = _shape(q)
+    _rows(q, (k, v))
+    _need(table, (FSA_TAP_TABLE_BYTES,), torch.uint8, "table")
+    out, flags = _out_buffer(out, out_dtype, (B, H, T, D), q.device, 0)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    _need(lse, (B, H, T), torch.float32, "lse")
+    st = lib().fsa_forward_dev(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, D,
+                               _ptr(table), int(window), flags, _ptr(out), _ptr(lse),
+                               _stream(stream))
+    _check("fsa_forward_dev", st)
+    return out, lse
+
+
+def fsa_backward_dev(q, k, v, dout, lse, table, window, dq=None, dk=None, dv=None,
+                     dalpha=None, workspace=None, stream=None):
+    """fsa_backward with the layer's tap table from device memory; dalpha is a
+    [1] fp32 device tensor (a view of one layer's slot is fine)."""
+    import torch
+    B, H, T, D = _shape(q)
+    _rows(q, (k, v, dout))
+    _need(table, (FSA_TAP_TABLE_BYTES,), torch.uint8, "table")
+    dt = _dtype_code(q)
+    f32 = torch.float32
+    mk = lambda: torch.empty((B, H, T, D), dtype=f32, device=q.device)
+    dq = mk() if dq is None else _need(dq, (B, H, T, D), f32, "dq")
+    dk = mk() if dk is None else _need(dk, (B, H, T, D), f32, "dk")
+    dv = mk() if dv is None else _need(dv, (B, H, T, D), f32, "dv")
+    _need(lse, (B, H, T), f32, "lse")
+    if dalpha is None:
+        dalpha = torch.empty(1, dtype=f32, device=q.device)
+    _need(dalpha, (1,), f32, "dalpha")
+    nbytes = fsa_backward_workspace_size(B, H, T, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, nbytes)
+    st = lib().fsa_backward_dev(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), dt,
+                                B, H, T, D, _ptr(table), int(window), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(dalpha), _ptr(workspace),
+                                _ws_bytes(workspace), _stream(stream))
+    _check("fsa_backward_dev", st)
+    return dq, dk, dv, dalpha

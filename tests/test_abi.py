@@ -261,3 +261,46 @@ def test_rope_binding_checks_buffers():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         F.fsa_rope(x, 10000.0)                              # not a device tensor
+
+
+def test_learned_alpha_argument_checks():
+    """The learned-alpha entry points reject bad arguments before any HIP call
+    (fake, never dereferenced pointers where a pointer must be non-null)."""
+    L = F.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    ok = dict(theta_map=F.FSA_THETA_CLAMP, window=12, pattern=F.FSA_PATTERN_FIB)
+    inv = F.FSA_ERR_INVALID_ARG
+    # layers out of range, bad map, window, pattern (the bf16-out bit is not a tap pattern)
+    assert L.fsa_theta_alpha(fake, 0, 0, 12, 0, fake, fake, None) == inv
+    assert L.fsa_theta_alpha(fake, 1025, 0, 12, 0, fake, fake, None) == inv
+    assert L.fsa_theta_alpha(fake, 4, 7, 12, 0, fake, fake, None) == inv
+    assert L.fsa_theta_alpha(fake, 4, 0, 0, 0, fake, fake, None) == inv
+    assert L.fsa_theta_alpha(fake, 4, 0, 12, F.FSA_OUT_BF16, fake, fake, None) == inv
+    assert L.fsa_theta_alpha(None, 4, 0, 12, 0, fake, fake, None) == inv
+    assert L.fsa_theta_alpha(fake, 4, 0, 12, 0, fake, ctypes.c_void_p((1 << 20) + 16), None) == inv
+    step = lambda **kw: L.fsa_theta_step(
+        kw.get("theta", fake), fake, kw.get("L", 4), kw.get("map", 0), kw.get("opt", 1),
+        kw.get("lr", 0.01), kw.get("b1", 0.9), kw.get("b2", 0.999), kw.get("eps", 1e-8),
+        kw.get("state", fake), 12, 0, fake, fake, None)
+    assert step(opt=2) == inv
+    assert step(lr=-1.0) == inv
+    assert step(lr=float("nan")) == inv
+    assert step(b1=1.0) == inv
+    assert step(b2=-0.1) == inv
+    assert step(eps=0.0) == inv
+    assert step(state=ctypes.c_void_p((1 << 20) + 4)) == inv
+    assert step(theta=None) == inv
+    del ok
+    # device-table attention calls: a table must be given and aligned; the
+    # forward's flags take only the bf16-out bit
+    q = fake
+    assert L.fsa_forward_dev(q, q, q, F.FSA_DTYPE_BF16, 1, 1, 16, 64, None, 12, 0, q, q,
+                             None) == inv
+    assert L.fsa_forward_dev(q, q, q, F.FSA_DTYPE_BF16, 1, 1, 16, 64, q, 12,
+                             F.FSA_MODE_ROUND, q, q, None) == inv
+    assert L.fsa_forward_dev(q, q, q, F.FSA_DTYPE_BF16, 1, 1, 16, 96, q, 12, 0, q, q,
+                             None) == F.FSA_ERR_UNSUPPORTED
+    assert L.fsa_backward_dev(q, q, q, q, q, F.FSA_DTYPE_BF16, 1, 1, 16, 64, None, 12,
+                              q, q, q, q, q, 1 << 20, None) == inv
+    assert L.fsa_backward_dev(q, q, q, q, q, F.FSA_DTYPE_BF16, 1, 1, 16, 64, q, 12,
+                              q, q, q, q, None, 0, None) == F.FSA_ERR_WORKSPACE
