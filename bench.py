@@ -344,6 +344,72 @@ class RopeStack:
     step = Stack.step
 
 
+class RopeLayerStack:
+    """A layer with RoPE, forward and backward, both ways, on seeded N(0,1)
+    rows drawn on the device before rotation:
+      separate: the RoPE pass on q and k, forward, backward (dq and dk/dv
+                stages), the inverse pass on dq and dk;
+      fused:    the RoPE pass on k, the forward turning its query tiles (and
+                writing the turned rows the backward reads), the backward
+                turning dq and dk back at store time.
+    `sets` buffer sets serve the layers in turn."""
+
+    def __init__(self, wl, torch, F, I, layers, sets, fused, window=12):
+        import ctypes
+        self.wl, self.layers = wl, layers
+        B, H, T, D = wl.B, wl.H, wl.T, wl.D
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(I.SEED_ROOT + 97 * wl.workload_id)
+        bf, f32 = torch.bfloat16, torch.float32
+        alphas = F.fsa_schedule(F.FSA_SCHEDULE_LINEAR, 16)
+        nbytes = F.fsa_backward_workspace_size(B, H, T, D, F.FSA_DTYPE_BF16)
+        self.sets = []
+        for c in range(sets):
+            draw = lambda: torch.randn((B, H, T, D), generator=gen, device="cuda").to(bf)
+            t = {"qp": draw(), "kp": draw(), "v": draw(), "dout": draw()}
+            for n in ("q", "k"):
+                t[n] = torch.empty_like(t["qp"])
+            for n in ("out", "dq", "dk", "dv", "dqp", "dkp"):
+                t[n] = torch.empty((B, H, T, D), dtype=f32, device="cuda")
+            t["lse"] = torch.empty((B, H, T), dtype=f32, device="cuda")
+            t["da"] = torch.empty(1, dtype=f32, device="cuda")
+            t["ws"] = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            self.sets.append(t)
+        lib = F.lib()
+        vp, fl = ctypes.c_void_p, ctypes.c_float
+        st = vp(torch.cuda.current_stream().cuda_stream)
+        base = fl(wl.rope_base)
+        dt = F.FSA_DTYPE_BF16
+        self.order = []
+        for l in range(layers):
+            t = self.sets[l % sets]
+            p = {n: vp(x.data_ptr()) for n, x in t.items()}
+            a = fl(float(alphas[l % 16]))
+            nws = t["ws"].numel()
+            rope = lambda x, y, tin, inv: ("rope" if not inv else "rope_inv", lib.fsa_rope,
+                                           (p[x], tin, B, H, T, D, base, None, inv, p[y], tin, st))
+            if fused:
+                self.order += [
+                    rope("kp", "k", dt, 0),
+                    ("fwd_rope", lib.fsa_forward_rope,
+                     (p["qp"], p["k"], p["v"], dt, B, H, T, D, a, window, 0, base, None,
+                      p["out"], p["lse"], p["q"], st)),
+                    ("bwd_rope", lib.fsa_backward_rope,
+                     (p["q"], p["k"], p["v"], p["dout"], p["lse"], dt, B, H, T, D, a, window,
+                      0, base, None, p["dqp"], p["dkp"], p["dv"], p["da"], p["ws"], nws, st))]
+            else:
+                self.order += [
+                    rope("qp", "q", dt, 0), rope("kp", "k", dt, 0),
+                    ("fwd", lib.fsa_forward, (p["q"], p["k"], p["v"], dt, B, H, T, D, a, window,
+                                              p["out"], p["lse"], st)),
+                    ("bwd", lib.fsa_backward, (p["q"], p["k"], p["v"], p["dout"], p["lse"], dt,
+                                               B, H, T, D, a, window, p["dq"], p["dk"],
+                                               p["dv"], p["da"], p["ws"], nws, st)),
+                    rope("dq", "dqp", F.FSA_DTYPE_F32, 1), rope("dk", "dkp", F.FSA_DTYPE_F32, 1)]
+
+    step = Stack.step
+
+
 class Events:
     """Timing events on the launch stream, created through HIP with
     hipEventDisableSystemFence (no cache writeback and invalidation at each
@@ -811,6 +877,20 @@ def main():
             res["rope"][key] = rope
             del st5
             torch.cuda.empty_cache()
+            # a layer with RoPE both ways: the separate passes, or the rotation
+            # fused where the rows sit in registers (only the key rows keep a pass)
+            both = {}
+            for fused in (False, True):
+                st6 = RopeLayerStack(w, torch, F, I, layers, sets, fused)
+                ms6, per6, _ = time_stack(st6, max(4, args.steps), max(2, args.warmup), torch)
+                both["fused" if fused else "separate"] = {
+                    "ms_per_layer": round(ms6 / layers, 4),
+                    "median_us": {n: round(v * 1e3, 3) for n, v in per6.items()}}
+                del st6
+                torch.cuda.empty_cache()
+            both["fused_over_separate"] = round(both["fused"]["ms_per_layer"]
+                                                / both["separate"]["ms_per_layer"], 4)
+            res["rope"][key]["layer_fwd_bwd"] = both
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline and oracle check", file=sys.stderr, flush=True)

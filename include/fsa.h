@@ -415,6 +415,38 @@ int fsa_rope(const void* x, int in_dtype, int B, int H, int T, int D,
              float base, const int32_t* pos0, int inverse, void* y,
              int out_dtype, void* stream);
 
+/*
+ * fsa_forward_rope, fsa_backward_rope -- the attention calls with RoPE fused
+ * where the rows sit in registers [DSFS: Methodology > Architecture and
+ * attention > Implementation (RoPE before the gather)], for bf16 rows
+ * (D = 64 or 128; other dtypes return FSA_ERR_UNSUPPORTED, and take the
+ * separate pass fsa_rope). Rotation as fsa_rope: pairs (m, m + D/2), angle
+ * p * base^(-2m/D), row t of batch entry b at position p = pos0[b] + t (pos0
+ * a device int32[B], 4-byte aligned, or NULL for p = t), base finite and > 1.
+ *   fsa_forward_rope: fsa_forward_ex with q_pre the query rows BEFORE rotation
+ *     (the kernel turns each query tile in fp32 and rounds it to bf16, nearest
+ *     even); k must already be rotated (fsa_rope). When q_rot is not NULL
+ *     (device bf16 [B][H][T][D], 16-byte aligned) the turned query rows are
+ *     written there, the rows fsa_backward_rope reads as q.
+ *   fsa_backward_rope: fsa_backward_ex on the rotated q and k, with dq_pre and
+ *     dk_pre the gradients with respect to the rows BEFORE rotation (the
+ *     kernels turn dq and dk back at store time, the transpose of the
+ *     rotation); dv and dalpha as fsa_backward_ex.
+ * Sines and cosines come from the hardware (argument in turns, reduced in
+ * fp64); other arguments, layouts and errors as fsa_forward_ex and
+ * fsa_backward_ex.
+ */
+int fsa_forward_rope(const void* q_pre, const void* k, const void* v, int dtype,
+                     int B, int H, int T, int D, float alpha, int window,
+                     int pattern, float base, const int32_t* pos0, void* out,
+                     float* lse, void* q_rot, void* stream);
+int fsa_backward_rope(const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, int dtype, int B, int H,
+                      int T, int D, float alpha, int window, int pattern,
+                      float base, const int32_t* pos0, float* dq_pre,
+                      float* dk_pre, float* dv, float* dalpha, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* fsa_status_string -- static text for a status code. */
 const char* fsa_status_string(int status);
 

@@ -352,6 +352,80 @@ int fsa_backward_ex(const void* q, const void* k, const void* v,
                             workspace_bytes, stream);
 }
 
+namespace {
+
+// Checks of the fused-RoPE calls beyond those of the plain ones: bf16 rows
+// (the tile kernels), a finite base above 1, pos0 4-byte aligned or null.
+int check_rope(int dtype, int D, float base, const int32_t* pos0) {
+  if (!std::isfinite(base) || !(base > 1.f)) return FSA_ERR_INVALID_ARG;
+  if (pos0 != nullptr && (reinterpret_cast<uintptr_t>(pos0) & 3u) != 0)
+    return FSA_ERR_INVALID_ARG;
+  if (dtype != FSA_DTYPE_BF16 || (D != 64 && D != 128)) return FSA_ERR_UNSUPPORTED;
+  return FSA_OK;
+}
+
+RopeArg rope_arg(float base, int D, const int32_t* pos0, void* q_out) {
+  RopeArg r{};
+  r.on = 1;
+  // as the RoPE pass forms them (fsa_rope), so that both turn by the same bits
+  r.log2_base = std::log2(static_cast<double>(base));
+  r.ratio = std::pow(static_cast<double>(base), -2.0 / D);
+  r.pos0 = pos0;
+  r.q_out = static_cast<uint16_t*>(q_out);
+  return r;
+}
+
+}  // namespace
+
+int fsa_forward_rope(const void* q_pre, const void* k, const void* v, int dtype,
+                     int B, int H, int T, int D, float alpha, int window,
+                     int pattern, float base, const int32_t* pos0, void* out,
+                     float* lse, void* q_rot, void* stream) {
+  if (!pattern_ok(pattern)) return FSA_ERR_INVALID_ARG;
+  int st = check_shape(dtype, B, H, T, D, alpha, window);
+  if (st != FSA_OK) return st;
+  if ((st = check_rope(dtype, D, base, pos0)) != FSA_OK) return st;
+  if (static_cast<long long>(B) * H * T == 0) return FSA_OK;
+  if (!q_pre || !k || !v || !out || !lse) return FSA_ERR_INVALID_ARG;
+  if (!aligned16(q_pre) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(lse) || (q_rot != nullptr && !aligned16(q_rot)))
+    return FSA_ERR_INVALID_ARG;
+  TapsArg taps{};
+  build_taps(pattern, alpha, window, &taps.v);
+  const Problem pr = make_problem(B, H, T, D, window);
+  return hip_status(launch_fwd_mfma(q_pre, k, v, pr, taps, out,
+                                    (pattern & FSA_OUT_BF16) != 0, lse,
+                                    static_cast<hipStream_t>(stream),
+                                    rope_arg(base, D, pos0, q_rot)));
+}
+
+int fsa_backward_rope(const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, int dtype, int B, int H,
+                      int T, int D, float alpha, int window, int pattern,
+                      float base, const int32_t* pos0, float* dq_pre,
+                      float* dk_pre, float* dv, float* dalpha, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int st = fsa::check_backward_call(q, k, v, dout, lse, dtype, B, H, T, D, alpha,
+                                    window, pattern, dq_pre, dk_pre, dv, dalpha,
+                                    &empty);
+  if (st != FSA_OK) return st;
+  if ((st = check_rope(dtype, D, base, pos0)) != FSA_OK) return st;
+  BwdArgs a;
+  st = check_bwd(q, k, v, dout, lse, dtype, B, H, T, D, alpha, window, pattern,
+                 workspace, workspace_bytes, &a);
+  if (st != FSA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.empty) return hip_status(launch_dalpha_reduce(nullptr, 0, dalpha, s));
+  const RopeArg rope = rope_arg(base, D, pos0, nullptr);
+  st = hip_status(launch_bwd_dq_mfma(q, k, v, dout, lse, a.pr, a.taps, dq_pre,
+                                     a.delta, a.partials, s, rope));
+  if (st != FSA_OK) return st;
+  return hip_status(launch_bwd_dkdv_mfma(q, k, v, dout, lse, a.delta, a.partials,
+                                         bwd_partials_used(a.pr, dtype), a.pr,
+                                         a.taps, dk_pre, dv, dalpha, s, rope));
+}
+
 int fsa_forward_dev(const void* q, const void* k, const void* v, int dtype,
                     int B, int H, int T, int D, const void* tap_table,
                     int window, int flags, void* out, float* lse, void* stream) {

@@ -37,6 +37,19 @@ __device__ __forceinline__ CTaps& taps_of(const TapsArg& a) {
   return a.dev ? *(CTaps*)a.dev : *(CTaps*)&a.v;
 }
 
+// RoPE fused into the bf16 tile kernels: the forward turns its query tile in
+// registers (and writes the turned rows when q_out is set), the backward
+// turns dq and dk back at store time (the transpose), so only the key rows
+// need a pass of their own. Row t of batch entry b stands at position
+// pos0[b] + t (t without pos0); frequencies base^(-2m/D), pairs (m, m + D/2).
+struct RopeArg {
+  int on;               // 0: the rows are already rotated; nothing is turned
+  double log2_base;     // log2 of the frequency base
+  double ratio;         // base^(-2/D): frequency m+1 over frequency m
+  const int* pos0;      // device int32[B], or null
+  uint16_t* q_out;      // forward: rotated q rows (bf16) written here if set
+};
+
 struct Problem {
   int B, H, T, D, W;
   float scale;  // 1/sqrt(D)
@@ -129,17 +142,20 @@ size_t bwd_partials_used_vec(const Problem& pr);
 bool mfma_supported(const Problem& pr, int dtype);
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
                            const Problem& pr, const TapsArg& taps, void* out,
-                           bool out_bf16, float* lse, hipStream_t s);
+                           bool out_bf16, float* lse, hipStream_t s,
+                           const RopeArg& rope = RopeArg{});
 hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               const void* dout, const float* lse,
                               const Problem& pr, const TapsArg& taps, float* dq,
-                              float* delta, float* partials, hipStream_t s);
+                              float* delta, float* partials, hipStream_t s,
+                              const RopeArg& rope = RopeArg{});
 hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
                                 const void* dout, const float* lse,
                                 const float* delta, const float* partials,
                                 size_t n_partials, const Problem& pr,
                                 const TapsArg& taps, float* dk, float* dv,
-                                float* dalpha, hipStream_t s);
+                                float* dalpha, hipStream_t s,
+                                const RopeArg& rope = RopeArg{});
 size_t bwd_partials_used_mfma(const Problem& pr);
 
 }  // namespace fsa

@@ -561,6 +561,95 @@ __device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, uint
   }
 }
 
+// ---------------------------------------------------------------- fused RoPE
+// The rotation before the gather (Depth-Staggered Fibonacci Spacing for Sparse
+// Attention, Methodology > Architecture and attention > Implementation) done
+// on rows the kernels hold in registers: the forward's query tile, and dq and
+// dk turned back at store time. Pairs (m, m + D/2), frequency base^(-2m/D),
+// row t of batch entry b at position pos0[b] + t.
+constexpr double kInv2Pi = 0.15915494309189533577;   // 1 / (2 pi)
+
+// Position of row 0 of slab bh.
+__device__ __forceinline__ long long rope_row0(const RopeArg& rope, int bh, int H) {
+  return rope.pos0 ? static_cast<long long>(rope.pos0[bh / H]) : 0LL;
+}
+
+// The angles of four consecutive frequencies m0..m0+3 (m0 a multiple of 4)
+// at position p, formed as the RoPE pass forms them so that both give the
+// same bits: theta_m0 = 2^(-(2 m0 / D) log2(base)), then times base^(-2/D)
+// for each next m, in fp64; the turn count p theta / (2 pi) reduced to
+// [-1/2, 1/2] in fp64; sine and cosine in fp32 of the reduced angle.
+template <int D>
+__device__ __forceinline__ void rope_angles4(int m0, double pd, const RopeArg& rope,
+                                             float* sn, float* cs) {
+  double theta = exp2(-(2.0 * m0 / D) * rope.log2_base);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    double rev = pd * theta * kInv2Pi;
+    rev -= rint(rev);
+    sincospif(static_cast<float>(2.0 * rev), &sn[j], &cs[j]);
+    theta *= rope.ratio;
+  }
+}
+
+// Turn the query tile held as B operands (lane (g, n): row n, elements
+// 32s + 8g + e of k-step s, e = 0..7) to position p: the pair (m, m + D/2) is
+// element e of steps s and s + D/64, m = 32s + 8g + e. Results are rounded
+// to bf16, nearest even.
+template <int D>
+__device__ __forceinline__ void rope_qtile(u32x4* qb, int g, long long p, const RopeArg& rope) {
+  constexpr int kHalf = D / 64;                        // k-steps per half row
+  const double pd = static_cast<double>(p);
+#pragma unroll
+  for (int s = 0; s < kHalf; ++s) {
+    float a[8], b[8], sn[8], cs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wa = qb[s][e >> 1], wb = qb[s + kHalf][e >> 1];
+      a[e] = __uint_as_float((e & 1) ? (wa & 0xffff0000u) : (wa << 16));
+      b[e] = __uint_as_float((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+    }
+    rope_angles4<D>(32 * s + 8 * g, pd, rope, sn, cs);
+    rope_angles4<D>(32 * s + 8 * g + 4, pd, rope, sn + 4, cs + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = a[e], y = b[e];
+      a[e] = fmaf(x, cs[e], -(y * sn[e]));             // the RoPE pass's rounding order
+      b[e] = fmaf(x, sn[e], y * cs[e]);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      qb[s][w] = pack_bf16(a[2 * w], a[2 * w + 1]);
+      qb[s + kHalf][w] = pack_bf16(b[2 * w], b[2 * w + 1]);
+    }
+  }
+}
+
+// Turn a result tile in the C layout of the products over rows (lane (g, n):
+// row n, columns 16mb + 4g + j of acc[mb]) by the angle sgn * p * theta_m; the
+// pair (m, m + D/2) is register j of acc[mb] and acc[mb + D/32],
+// m = 16mb + 4g + j. sgn = -1 is the transpose: it maps a gradient with
+// respect to rotated rows to the gradient with respect to the rows before
+// rotation.
+template <int D>
+__device__ __forceinline__ void rope_tile(f32x4* acc, int g, long long p, const RopeArg& rope,
+                                          float sgn) {
+  constexpr int kHalf = D / 32;
+  const double pd = static_cast<double>(p);
+#pragma unroll
+  for (int mb = 0; mb < kHalf; ++mb) {
+    float sn[4], cs[4];
+    rope_angles4<D>(16 * mb + 4 * g, pd, rope, sn, cs);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = sn[j] * sgn;
+      const float x = acc[mb][j], y = acc[mb + kHalf][j];
+      acc[mb][j] = fmaf(x, cs[j], -(y * s));           // the RoPE pass's rounding order
+      acc[mb + kHalf][j] = fmaf(x, s, y * cs[j]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- forward
 // One wavefront per 15-query tile. Key blocks are taken in pairs: the window
 // pairs first, then the tap pairs; K and V of a pair are staged in the
@@ -574,11 +663,11 @@ __device__ __forceinline__ void store_tile(lds_char* buf, const f32x4* acc, uint
 // query n's score, and m is raised only when a score passes it by more than
 // 2^kLazy (weights up to 2^kLazy are summed as they are): the rescale of the
 // accumulators is then rare, and l, the output and lse stay exact.
-template <int D, typename OutT>
+template <int D, typename OutT, bool kRope>
 __global__ __launch_bounds__(64) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Problem pr, TapsArg taps_arg, int n_tiles, int hg,
-    OutT* __restrict__ out, float* __restrict__ lse) {
+    OutT* __restrict__ out, float* __restrict__ lse, RopeArg rope) {
   CTaps& taps = taps_of(taps_arg);
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;         // K_x K_y V_x V_y
@@ -626,6 +715,16 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
       stage_two<D>(sk, sv, tl, i0 - 32 * p, 2 * p + 1 < nwb ? i0 - 32 * p - 16 : INT_MIN, lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
+    if (kRope && p == 0) {
+      // the tile's rows have arrived: turn them, and hand the turned rows on
+      rope_qtile<D>(qb, g, rope_row0(rope, bh, pr.H) + i, rope);
+      if (rope.q_out != nullptr && qvalid) {
+        uint16_t* dst = rope.q_out + base + static_cast<size_t>(i) * D + 8 * g;
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st)
+          __builtin_nontemporal_store(qb[st], reinterpret_cast<u32x4*>(dst + 32 * st));
+      }
+    }
     float sc[2][4];
     float lmax = -INFINITY;
 #pragma unroll
@@ -744,13 +843,13 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
 //   -f * [dS * scale * q.(K[a+1]-K[a]) + p * dout.(V[a+1]-V[a])]
 // = A - Delta_i * B with A and B accumulated per lane. The wavefront writes
 // Delta_i, dq, and one dalpha partial.
-template <int D>
+template <int D, bool kRope>
 __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, Problem pr, TapsArg taps_arg, int n_tiles, int hg,
     float* __restrict__ dq, float* __restrict__ delta,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, RopeArg rope) {
   CTaps& taps = taps_of(taps_arg);
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // K_x K_y V_x V_y
@@ -907,6 +1006,8 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) a1[mb][j] = scale * (a1[mb][j] - Dl * a2[mb][j]);
+  if (kRope)                          // the gradient of the rows before rotation
+    rope_tile<D>(a1, g, rope_row0(rope, bh, pr.H) + i, rope, -1.f);
   store_tile<D>(lds, a1, dq + base + static_cast<size_t>(i0) * D, lane,
                 [&](int r) { return r < kTileQ && i0 + r < T; });
   if (qvalid && g == 0)
@@ -950,14 +1051,14 @@ __device__ __forceinline__ TapSel key_tap_sel(int n, int g) {
 
 // Register budget: five wavefronts per SIMD at D = 64 (96 VGPRs), three at
 // D = 128 (164 VGPRs; two, at 171, took 5-8% longer at T = 65536).
-template <int D>
+template <int D, bool kRope>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 3))) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ partials, int n_partials, Problem pr, TapsArg taps_arg,
     int n_tiles, float* __restrict__ dk, float* __restrict__ dv,
-    float* __restrict__ dalpha) {
+    float* __restrict__ dalpha, RopeArg rope) {
   CTaps& taps = taps_of(taps_arg);
   using Tl = Tile<D>;
   constexpr int kStage = 4 * Tl::kBlockBytes;          // Q_x Q_y G_x G_y
@@ -1159,16 +1260,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 
     __builtin_amdgcn_wave_barrier();
   }
 
+  // rows 1 .. kTileK of the block are this tile's keys (0 and 15 are halos);
+  // dv first, so that its accumulators are free while dk is scaled (and
+  // turned back when RoPE is fused)
+  auto key_ok = [&](int r) { return r >= 1 && r <= kTileK && rowb + r < T; };
+  store_tile<D>(lds, av, dv + base + static_cast<size_t>(rowb) * D, lane, key_ok);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) ak[mb][j] *= scale;
-  // rows 1 .. kTileK of the block are this tile's keys (0 and 15 are halos)
-  auto key_ok = [&](int r) { return r >= 1 && r <= kTileK && rowb + r < T; };
+  if (kRope)                          // the gradient of the rows before rotation
+    rope_tile<D>(ak, g, rope_row0(rope, bh, pr.H) + r, rope, -1.f);
   store_tile<D>(lds, ak, dk + base + static_cast<size_t>(rowb) * D, lane, key_ok);
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  store_tile<D>(lds, av, dv + base + static_cast<size_t>(rowb) * D, lane, key_ok);
 }
 
 }  // namespace
@@ -1189,7 +1294,8 @@ static int head_group(const Problem& pr, int cap) {
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
                            const Problem& pr, const TapsArg& taps, void* out,
-                           bool out_bf16, float* lse, hipStream_t s) {
+                           bool out_bf16, float* lse, hipStream_t s,
+                           const RopeArg& rope) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
   const int hg = head_group(pr, 8);
@@ -1198,21 +1304,23 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v,
   const auto* vv = static_cast<const uint16_t*>(v);
   auto* of = static_cast<float*>(out);
   auto* ob = static_cast<uint16_t*>(out);
+#define FSA_FWD(DD, OT, R, O)                                                     \
+  hipLaunchKernelGGL((fwd_mfma_kernel<DD, OT, R>), grid, dim3(64), 0, s, qq, kk, vv, \
+                     pr, taps, n_tiles, hg, O, lse, rope)
   if (pr.D == 64) {
-    if (out_bf16)
-      hipLaunchKernelGGL((fwd_mfma_kernel<64, uint16_t>), grid, dim3(64), 0, s, qq, kk, vv, pr,
-                         taps, n_tiles, hg, ob, lse);
-    else
-      hipLaunchKernelGGL((fwd_mfma_kernel<64, float>), grid, dim3(64), 0, s, qq, kk, vv, pr,
-                         taps, n_tiles, hg, of, lse);
+    if (rope.on) {
+      if (out_bf16) FSA_FWD(64, uint16_t, true, ob); else FSA_FWD(64, float, true, of);
+    } else {
+      if (out_bf16) FSA_FWD(64, uint16_t, false, ob); else FSA_FWD(64, float, false, of);
+    }
   } else {
-    if (out_bf16)
-      hipLaunchKernelGGL((fwd_mfma_kernel<128, uint16_t>), grid, dim3(64), 0, s, qq, kk, vv, pr,
-                         taps, n_tiles, hg, ob, lse);
-    else
-      hipLaunchKernelGGL((fwd_mfma_kernel<128, float>), grid, dim3(64), 0, s, qq, kk, vv, pr,
-                         taps, n_tiles, hg, of, lse);
+    if (rope.on) {
+      if (out_bf16) FSA_FWD(128, uint16_t, true, ob); else FSA_FWD(128, float, true, of);
+    } else {
+      if (out_bf16) FSA_FWD(128, uint16_t, false, ob); else FSA_FWD(128, float, false, of);
+    }
   }
+#undef FSA_FWD
   return hipGetLastError();
 }
 
@@ -1227,7 +1335,8 @@ size_t bwd_partials_used_mfma(const Problem& pr) {
 hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               const void* dout, const float* lse,
                               const Problem& pr, const TapsArg& taps, float* dq,
-                              float* delta, float* partials, hipStream_t s) {
+                              float* delta, float* partials, hipStream_t s,
+                              const RopeArg& rope) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
   const int hg = head_group(pr, 2);
@@ -1235,12 +1344,15 @@ hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   const auto* gg = static_cast<const uint16_t*>(dout);
-  if (pr.D == 64)
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<64>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, pr, taps, n_tiles, hg, dq, delta, partials);
-  else
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<128>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, pr, taps, n_tiles, hg, dq, delta, partials);
+#define FSA_DQ(DD, R)                                                                  \
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<DD, R>), grid, dim3(64), 0, s, qq, kk, vv, gg, \
+                     lse, pr, taps, n_tiles, hg, dq, delta, partials, rope)
+  if (pr.D == 64) {
+    if (rope.on) FSA_DQ(64, true); else FSA_DQ(64, false);
+  } else {
+    if (rope.on) FSA_DQ(128, true); else FSA_DQ(128, false);
+  }
+#undef FSA_DQ
   return hipGetLastError();
 }
 
@@ -1249,21 +1361,23 @@ hipError_t launch_bwd_dkdv_mfma(const void* q, const void* k, const void* v,
                                 const float* delta, const float* partials,
                                 size_t n_partials, const Problem& pr,
                                 const TapsArg& taps, float* dk, float* dv,
-                                float* dalpha, hipStream_t s) {
+                                float* dalpha, hipStream_t s, const RopeArg& rope) {
   const int n_tiles = (pr.T + kTileK - 1) / kTileK;
   const dim3 grid(n_tiles * pr.B * pr.H);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   const auto* gg = static_cast<const uint16_t*>(dout);
-  if (pr.D == 64)
-    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<64>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, delta, partials, static_cast<int>(n_partials), pr,
-                       taps, n_tiles, dk, dv, dalpha);
-  else
-    hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<128>, grid, dim3(64), 0, s, qq, kk, vv,
-                       gg, lse, delta, partials, static_cast<int>(n_partials), pr,
-                       taps, n_tiles, dk, dv, dalpha);
+  const int np = static_cast<int>(n_partials);
+#define FSA_DKDV(DD, R)                                                                  \
+  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<DD, R>), grid, dim3(64), 0, s, qq, kk, vv, gg, \
+                     lse, delta, partials, np, pr, taps, n_tiles, dk, dv, dalpha, rope)
+  if (pr.D == 64) {
+    if (rope.on) FSA_DKDV(64, true); else FSA_DKDV(64, false);
+  } else {
+    if (rope.on) FSA_DKDV(128, true); else FSA_DKDV(128, false);
+  }
+#undef FSA_DKDV
   return hipGetLastError();
 }
 

@@ -124,8 +124,10 @@ __global__ __launch_bounds__(kRopeBlock) void rope_kernel(
       float ya[kPairsPerThread], yb[kPairsPerThread];
 #pragma unroll
       for (int j = 0; j < kPairsPerThread; ++j) {
-        ya[j] = xa[h][j] * cs[j] - xb[h][j] * sn[j];
-        yb[j] = xa[h][j] * sn[j] + xb[h][j] * cs[j];
+        // one rounding order, written out (the fused rotation in the
+        // attention kernels uses the same, so both give the same bits)
+        ya[j] = fmaf(xa[h][j], cs[j], -(xb[h][j] * sn[j]));
+        yb[j] = fmaf(xa[h][j], sn[j], xb[h][j] * cs[j]);
       }
       store4(y + off0 + h * slab, ya);
       store4(y + off0 + h * slab + half, yb);

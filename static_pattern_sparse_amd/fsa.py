@@ -61,7 +61,7 @@ EXPORTS = ("fsa_schedule", "fsa_offsets", "fsa_offsets_ex", "fsa_forward",
            "fsa_backward_ex", "fsa_backward_dq", "fsa_backward_dq_ex",
            "fsa_backward_dkdv", "fsa_backward_dkdv_ex", "fsa_backward_noalloc",
            "fsa_decode", "fsa_theta_alpha", "fsa_theta_step", "fsa_forward_dev",
-           "fsa_backward_dev",
+           "fsa_backward_dev", "fsa_forward_rope", "fsa_backward_rope",
            "fsa_rope", "fsa_status_string", "fsa_last_hip_error")
 
 _lib = None
@@ -133,6 +133,13 @@ def lib():
     L.fsa_backward_dev.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
                                    i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.fsa_backward_dev.restype = i32
+    L.fsa_forward_rope.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                   f32, vp, vp, vp, vp, vp]
+    L.fsa_forward_rope.restype = i32
+    L.fsa_backward_rope.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                    i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_size_t, vp]
+    L.fsa_backward_rope.restype = i32
     L.fsa_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, i32,
                              i32, vp, vp, vp]
     L.fsa_decode.restype = i32
@@ -505,4 +512,66 @@ def fsa_backward_dev(q, k, v, dout, lse, table, window, dq=None, dk=None, dv=Non
                                 _ptr(dv), _ptr(dalpha), _ptr(workspace),
                                 _ws_bytes(workspace), _stream(stream))
     _check("fsa_backward_dev", st)
+    return dq, dk, dv, dalpha
+
+
+# ------------------------------------------------------------- fused RoPE
+def fsa_forward_rope(q_pre, k, v, alpha, window, base, pos0=None, out=None, lse=None,
+                     q_rot=None, stream=None, pattern=FSA_PATTERN_FIB, out_dtype=None,
+                     want_q_rot=True):
+    """fsa_forward with the query rows given before RoPE (bf16): the kernel
+    turns each query tile; k must already be rotated. Returns (out, lse,
+    q_rot) with q_rot the turned query rows (bf16), or None when
+    want_q_rot is False."""
+    import torch
+    B, H, T, D = _shape(q_pre)
+    _rows(q_pre, (k, v))
+    out, flags = _out_buffer(out, out_dtype, (B, H, T, D), q_pre.device, pattern)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q_pre.device)
+    _need(lse, (B, H, T), torch.float32, "lse")
+    if want_q_rot and q_rot is None:
+        q_rot = torch.empty_like(q_pre)
+    if q_rot is not None:
+        _need(q_rot, (B, H, T, D), q_pre.dtype, "q_rot")
+    if pos0 is not None:
+        _need(pos0, (B,), torch.int32, "pos0")
+    st = lib().fsa_forward_rope(_ptr(q_pre), _ptr(k), _ptr(v), _dtype_code(q_pre), B, H,
+                                T, D, float(alpha), int(window), flags, float(base),
+                                _ptr(pos0), _ptr(out), _ptr(lse), _ptr(q_rot),
+                                _stream(stream))
+    _check("fsa_forward_rope", st)
+    return out, lse, q_rot
+
+
+def fsa_backward_rope(q, k, v, dout, lse, alpha, window, base, pos0=None, dq=None,
+                      dk=None, dv=None, dalpha=None, workspace=None, stream=None,
+                      pattern=FSA_PATTERN_FIB):
+    """fsa_backward on rotated q, k (bf16), with dq and dk returned as the
+    gradients with respect to the rows before rotation."""
+    import torch
+    B, H, T, D = _shape(q)
+    _rows(q, (k, v, dout))
+    dt = _dtype_code(q)
+    f32 = torch.float32
+    mk = lambda: torch.empty((B, H, T, D), dtype=f32, device=q.device)
+    dq = mk() if dq is None else _need(dq, (B, H, T, D), f32, "dq")
+    dk = mk() if dk is None else _need(dk, (B, H, T, D), f32, "dk")
+    dv = mk() if dv is None else _need(dv, (B, H, T, D), f32, "dv")
+    _need(lse, (B, H, T), f32, "lse")
+    if dalpha is None:
+        dalpha = torch.empty(1, dtype=f32, device=q.device)
+    _need(dalpha, (1,), f32, "dalpha")
+    if pos0 is not None:
+        _need(pos0, (B,), torch.int32, "pos0")
+    nbytes = fsa_backward_workspace_size(B, H, T, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, nbytes)
+    st = lib().fsa_backward_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), dt,
+                                 B, H, T, D, float(alpha), int(window), int(pattern),
+                                 float(base), _ptr(pos0), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(dalpha), _ptr(workspace), _ws_bytes(workspace),
+                                 _stream(stream))
+    _check("fsa_backward_rope", st)
     return dq, dk, dv, dalpha

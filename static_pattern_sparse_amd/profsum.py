@@ -33,8 +33,15 @@ def kernel_label(full):
     if not inner:
         return name
     args = [a.strip() for a in inner.split(",")]
-    if name == "fwd_mfma_kernel" and args[-1] == "float":
+    # the fused-RoPE flag of the tile kernels: dropped when false, "rope" when true
+    rope = False
+    if args and args[-1] in ("true", "false"):
+        rope = args[-1] == "true"
         args = args[:-1]
+    if name == "fwd_mfma_kernel" and args and args[-1] == "float":
+        args = args[:-1]
+    if rope:
+        args.append("rope")
     return name + "<" + ",".join(_TYPES.get(a, a) for a in args) + ">"
 
 

@@ -304,3 +304,22 @@ def test_learned_alpha_argument_checks():
                               q, q, q, q, q, 1 << 20, None) == inv
     assert L.fsa_backward_dev(q, q, q, q, q, F.FSA_DTYPE_BF16, 1, 1, 16, 64, q, 12,
                               q, q, q, q, None, 0, None) == F.FSA_ERR_WORKSPACE
+
+
+def test_fused_rope_argument_checks():
+    """fsa_forward_rope / fsa_backward_rope: bf16 rows only (the tile kernels),
+    a finite base above 1, an aligned pos0; rejected before any HIP call."""
+    L = F.lib()
+    p = ctypes.c_void_p(1 << 20)
+    bf, f32 = F.FSA_DTYPE_BF16, F.FSA_DTYPE_F32
+    fwd = lambda dt=bf, D=64, base=10000.0, pos0=None: L.fsa_forward_rope(
+        p, p, p, dt, 1, 1, 16, D, 1.0, 8, 0, base, pos0, p, p, None, None)
+    assert fwd(dt=f32) == F.FSA_ERR_UNSUPPORTED
+    assert fwd(D=96) == F.FSA_ERR_UNSUPPORTED
+    assert fwd(base=1.0) == F.FSA_ERR_INVALID_ARG
+    assert fwd(base=float("inf")) == F.FSA_ERR_INVALID_ARG
+    assert fwd(pos0=ctypes.c_void_p((1 << 20) + 2)) == F.FSA_ERR_INVALID_ARG
+    bwd = lambda dt=bf, base=10000.0: L.fsa_backward_rope(
+        p, p, p, p, p, dt, 1, 1, 16, 64, 1.0, 8, 0, base, None, p, p, p, p, p, 1 << 20, None)
+    assert bwd(dt=f32) == F.FSA_ERR_UNSUPPORTED
+    assert bwd(base=0.5) == F.FSA_ERR_INVALID_ARG

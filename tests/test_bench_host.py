@@ -72,3 +72,8 @@ def test_kernel_labels():
     assert profsum.kernel_label("fwd_mfma_kernel<128, unsigned short>(x)").startswith("fwd_mfma_kernel<128,")
     assert profsum.kernel_label("bwd_dkdv_mfma_kernel<64>(a, b)") == "bwd_dkdv_mfma_kernel<64>"
     assert profsum.kernel_label("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+    # the fused-RoPE flag of the tile kernels
+    assert profsum.kernel_label("fsa::fwd_mfma_kernel<64, float, false>(x)") == "fwd_mfma_kernel<64>"
+    assert profsum.kernel_label("fsa::fwd_mfma_kernel<64, float, true>(x)") == "fwd_mfma_kernel<64,rope>"
+    assert profsum.kernel_label("bwd_dq_mfma_kernel<128, false>(a)") == "bwd_dq_mfma_kernel<128>"
+    assert profsum.kernel_label("bwd_dkdv_mfma_kernel<64, true>(a)") == "bwd_dkdv_mfma_kernel<64,rope>"
