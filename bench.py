@@ -688,6 +688,29 @@ def roofline(stack, per_ms, kernels, traffic_ok):
             "median_launch_us": kernels[dom]["median_us"]}
 
 
+def learned_leg(stack, res, args, wl, ms_step, torch, F):
+    """The learned-alpha step (every layer's forward and backward reading its
+    tap table from device memory, then one fsa_theta_step) on the static
+    stack's buffers; the static launches are restored afterwards and one
+    static step refreshes the results the oracle check reads."""
+    stack.prepare_learned(torch, F, F.FSA_THETA_CLAMP, F.FSA_OPT_ADAM)
+
+    ms_l, per_l, _ = time_stack(stack, args.steps, args.warmup, torch)
+    alphas_now = stack.l_alpha.cpu().numpy()
+    res["learned"] = {
+        "workload": wl.name + " (learned alpha: clip map, Adam, theta from alpha = 1)",
+        "ms_per_step": round(ms_l, 4), "static_ms_per_step": round(ms_step, 4),
+        "ratio_to_static": round(ms_l / ms_step, 4),
+        "value": round(args.layers * wl.B * wl.H * wl.T / (ms_l * 1e-3), 1),
+        "median_us": {n: round(v * 1e3, 3) for n, v in per_l.items()},
+        "alpha_range_after": [round(float(alphas_now.min()), 6), round(float(alphas_now.max()), 6)]}
+    # back to the static schedule; one more static step refreshes the results
+    # that the oracle check reads
+    stack._prepare_calls(torch, F)
+    stack.step()
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -700,6 +723,11 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-t65536", action="store_true")
     ap.add_argument("--skip-rope", action="store_true")
+    ap.add_argument("--skip-learned", action="store_true",
+                    help="leave out the learned-alpha step")
+    ap.add_argument("--skip-sweep", action="store_true",
+                    help="leave out the T4096 window sweep (other tap counts on the "
+                         "same grid, which counter runs would mix in)")
     ap.add_argument("--out-bf16", action="store_true",
                     help="the forward writes out in bf16 (FSA_OUT_BF16)")
     ap.add_argument("--pattern", default="fib",
@@ -765,21 +793,8 @@ def main():
     }
     # the learned-alpha step on the same buffers (Adam on theta with the clip
     # map): the layers' tables on the device, one update launch per step
-    stack.prepare_learned(torch, F, F.FSA_THETA_CLAMP, F.FSA_OPT_ADAM)
-    ms_l, per_l, _ = time_stack(stack, args.steps, args.warmup, torch)
-    alphas_now = stack.l_alpha.cpu().numpy()
-    res["learned"] = {
-        "workload": wl.name + " (learned alpha: clip map, Adam, theta from alpha = 1)",
-        "ms_per_step": round(ms_l, 4), "static_ms_per_step": round(ms_step, 4),
-        "ratio_to_static": round(ms_l / ms_step, 4),
-        "value": round(args.layers * wl.B * wl.H * wl.T / (ms_l * 1e-3), 1),
-        "median_us": {n: round(v * 1e3, 3) for n, v in per_l.items()},
-        "alpha_range_after": [round(float(alphas_now.min()), 6), round(float(alphas_now.max()), 6)]}
-    # back to the static schedule; one more static step refreshes the results
-    # that the oracle check reads
-    stack._prepare_calls(torch, F)
-    stack.step()
-    torch.cuda.synchronize()
+    if not args.skip_learned:
+        learned_leg(stack, res, args, wl, ms_step, torch, F)
     # the first and the last layer's GPU results, for the oracle check that
     # runs with the CPU baseline after every GPU leg
     snap1024 = stack.snapshot((0, args.layers - 1)) if not args.no_cpu_baseline else None
@@ -803,7 +818,7 @@ def main():
         # the window sweep of the same stack: forward launches only (the
         # inputs do not depend on W), host clock over back-to-back launches
         sweep = {}
-        for W in (6, 8, 10, 12):
+        for W in (() if args.skip_sweep else (6, 8, 10, 12)):
             st2.W = W
             st2._prepare_calls(torch, F)
             fwd = [(fn, a) for name, fn, a in st2.order if name == "fwd"]
@@ -820,7 +835,8 @@ def main():
             ab = algo_bytes(wl2.D, 2, st2.out_bytes)["fwd"] * wl2.B * wl2.H * wl2.T
             sweep[f"W{W}"] = {"fwd_us": round(us, 2),
                               "hbm_frac": round(ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        res["t4096"]["window_sweep_forward"] = sweep
+        if sweep:
+            res["t4096"]["window_sweep_forward"] = sweep
         del st2
         torch.cuda.empty_cache()
 
