@@ -217,6 +217,8 @@ class Stack:
             st = fn(*args)
             if st != 0:
                 raise RuntimeError(f"{name} returned status {st}")
+            if ev is not None:
+                ev.record(Events.END)
         if ev is not None:
             ev.record(None)
 
@@ -413,11 +415,15 @@ class RopeLayerStack:
 class Events:
     """Timing events on the launch stream, created through HIP with
     hipEventDisableSystemFence (no cache writeback and invalidation at each
-    record). The time from the event before a launch to the next event is that
-    launch's time. All events are created up front, so recording one costs the
-    host only the enqueue."""
+    record). Each launch is bracketed by an event before it and an event
+    after it; the time between the two is that launch's time. Every record
+    costs the command processor a few microseconds, and an event-to-event
+    gap taken from one launch to the next would add that cost to every
+    launch; with the pair it falls between launches instead. All events are
+    created up front, so recording one costs the host only the enqueue."""
 
     DISABLE_SYSTEM_FENCE = 0x20000000
+    END = ""                          # the event after a launch
 
     def __init__(self, torch, count):
         import ctypes
@@ -434,24 +440,27 @@ class Events:
         self.marks = []
 
     def record(self, name):
+        """An event before a launch (`name` = the launch's kernel), after it
+        (END) or at the end of a step (None)."""
         e = self.pool[len(self.marks)]
         if self.hip.hipEventRecord(e, self.stream) != 0:
             raise RuntimeError("hipEventRecord failed")
         self.marks.append((name, e))
 
     def per_kernel_ms(self, skip_steps=1):
-        """Median event-to-event time of each kernel over the recorded steps
-        after the first `skip_steps` ones, and the launches counted. The
-        median, not the mean: a host stall that drains the queue lands in
-        whichever gap it falls in and would move a mean by its whole length."""
+        """Median time of each kernel from the event before its launch to the
+        event after it, over the recorded steps after the first `skip_steps`
+        ones, and the launches counted. The median, not the mean: a host stall
+        that drains the queue lands in whichever launch it falls in and would
+        move a mean by its whole length."""
         gaps = {}
         f = self.ct.c_float()
         step = 0
-        for (name, e0), (_, e1) in zip(self.marks, self.marks[1:]):
+        for (name, e0), (nxt, e1) in zip(self.marks, self.marks[1:]):
             if name is None:
                 step += 1
                 continue
-            if step < skip_steps:
+            if name == self.END or nxt != self.END or step < skip_steps:
                 continue
             if self.hip.hipEventElapsedTime(self.ct.byref(f), e0, e1) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
@@ -479,7 +488,7 @@ def time_stack(stack, steps, warmup, torch):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    ev = Events(torch, (steps + 1) * (len(stack.order) + 1))
+    ev = Events(torch, (steps + 1) * (2 * len(stack.order) + 1))
     for _ in range(steps + 1):
         stack.step(ev)
     torch.cuda.synchronize()
@@ -492,8 +501,9 @@ def time_stack(stack, steps, warmup, torch):
 def consistency(ms_step, per_ms, per_step):
     """Self-check of the per-kernel figures: the kernel medians times their
     launches per step, summed, against the host-clock step time. The two
-    measure the same launches (the event gaps include the gaps between
-    kernels), so they must agree; a ratio outside 0.9-1.1 flags the line."""
+    measure the same launches; the kernel times leave out the short gaps
+    between one launch's end and the next one's start, so the sum sits a few
+    percent under the step time. A ratio outside 0.9-1.1 flags the line."""
     total = sum(per_ms[n] * per_step[n] for n in per_ms)
     ratio = total / ms_step if ms_step > 0 else float("nan")
     return {"sum_kernel_ms": round(total, 4), "ms_per_step": round(ms_step, 4),

@@ -77,3 +77,35 @@ def test_kernel_labels():
     assert profsum.kernel_label("fsa::fwd_mfma_kernel<64, float, true>(x)") == "fwd_mfma_kernel<64,rope>"
     assert profsum.kernel_label("bwd_dq_mfma_kernel<128, false>(a)") == "bwd_dq_mfma_kernel<128>"
     assert profsum.kernel_label("bwd_dkdv_mfma_kernel<64, true>(a)") == "bwd_dkdv_mfma_kernel<64,rope>"
+
+
+class _FakeHip:
+    """Stands in for the HIP runtime: an event is a host timestamp in ms."""
+
+    def __init__(self, ct):
+        self.ct = ct
+
+    def hipEventElapsedTime(self, out, e0, e1):
+        out._obj.value = e1 - e0
+        return 0
+
+
+def test_event_pairs_time_each_launch_alone():
+    """A launch's time runs from the event before it to the event after it;
+    the gap from one launch's end to the next launch's start (where the
+    records' own cost falls) counts for neither, and the first step is
+    dropped."""
+    import ctypes
+    ev = object.__new__(bench.Events)
+    ev.ct, ev.hip = ctypes, _FakeHip(ctypes)
+    END = bench.Events.END
+    marks, t = [], 0.0
+    for step, (a, b) in enumerate(((9.0, 9.0), (1.0, 2.0), (1.5, 2.5), (1.0, 3.0))):
+        for name, dur in (("fwd", a), ("bwd", b)):
+            marks.append((name, t)); t += dur
+            marks.append((END, t)); t += 3.3          # record cost between launches
+        marks.append((None, t))
+    ev.marks = marks
+    med, counts = ev.per_kernel_ms(skip_steps=1)
+    assert counts == {"fwd": 3, "bwd": 3}
+    assert abs(med["fwd"] - 1.0) < 1e-12 and abs(med["bwd"] - 2.5) < 1e-12
