@@ -131,7 +131,10 @@ def counter_metrics(paths):
       l1_to_l2_bytes_per_token_head  TCP_TCC_READ_REQ x 128 B / token-heads
       td_busy, td_stalled_on_tc      per texture-data unit, as fractions of
                               the kernel's cycles (GRBM_GUI_ACTIVE is summed
-                              over the 8 XCDs)"""
+                              over the 8 XCDs)
+      tcp_pending_stall       TCP_PENDING_STALL_CYCLES per L1, the same
+                              fraction (the L1 stalled on misses in flight)
+      ta_busy                 TA_BUSY_avr, the same fraction"""
     c = _counters(paths)
     out = {}
     for key, d in c.items():
@@ -148,6 +151,10 @@ def counter_metrics(paths):
             cyc = d["GRBM_GUI_ACTIVE"] / 8.0
             m["td_busy"] = d["TD_TD_BUSY_sum"] / N_CU / cyc
             m["td_stalled_on_tc"] = d["TD_TC_STALL_sum"] / N_CU / cyc
+        if d.get("GRBM_GUI_ACTIVE") and d.get("TCP_PENDING_STALL_CYCLES_sum") is not None:
+            m["tcp_pending_stall"] = d["TCP_PENDING_STALL_CYCLES_sum"] / N_CU / (d["GRBM_GUI_ACTIVE"] / 8.0)
+        if d.get("GRBM_GUI_ACTIVE") and d.get("TA_BUSY_avr") is not None:
+            m["ta_busy"] = d["TA_BUSY_avr"] / (d["GRBM_GUI_ACTIVE"] / 8.0)
         out[key] = m
     return out
 
