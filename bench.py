@@ -95,7 +95,8 @@ def algo_bytes(D, in_bytes, out_bytes=4):
 class Stack:
     """Device buffers of every layer of one workload."""
 
-    def __init__(self, wl, window, layers, torch, F, I, pattern="fib", out_bf16=False):
+    def __init__(self, wl, window, layers, torch, F, I, pattern="fib", out_bf16=False,
+                 seed_root=None):
         self.torch, self.F = torch, F
         self.wl, self.W, self.layers = wl, window, layers
         self.pattern = F.PATTERNS[pattern]
@@ -108,9 +109,11 @@ class Stack:
         dev = "cuda"
         self.L = []
         self.host = []                 # the layers' host inputs (oracle checks)
-        ws_bytes = F.fsa_backward_workspace_size(B, H, T, D, F.FSA_DTYPE_BF16)
+        dt = F.FSA_DTYPE_BF16 if wl.dtype == "bf16" else F.FSA_DTYPE_F32
+        ws_bytes = F.fsa_backward_workspace_size(B, H, T, D, dt)
+        seed = I.SEED_ROOT if seed_root is None else seed_root
         for l in range(layers):
-            x = I.workload_inputs(wl, l)
+            x = I.workload_inputs(wl, l, seed_root=seed)
             self.host.append(x)
             t = {n: I.to_device(x[n], wl.dtype) for n in ("q", "k", "v", "dout")}
             f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
@@ -621,11 +624,12 @@ def _noop(_):
     return os.getpid()
 
 
-def cpu_baseline(stack, pattern="fib", passes=2):
+def cpu_baseline(stack, pattern="fib", passes=2, per_slab=False):
     """The fp64 oracle (forward + backward of every (b, h) slab) over every
-    layer of the stack, one layer per worker task, `passes` times over the
-    step; timed as a reported baseline. On its first pass the results of the
-    layers whose GPU results the snapshot holds are compared with them
+    layer of the stack, `passes` times over the step, one layer per worker
+    task (or one (b, h) slab per task with `per_slab`, for a single long
+    layer); timed as a reported baseline. On its first pass the results of
+    the layers whose GPU results the snapshot holds are compared with them
     (outside any timed GPU region). `stack` is a Stack.snapshot()."""
     wl, layers = stack.wl, stack.layers
     check_layers = tuple(stack.got)
@@ -634,13 +638,20 @@ def cpu_baseline(stack, pattern="fib", passes=2):
         os.environ[var] = "1"
     base, _, mode = pattern.partition("-")
     mode = "round" if mode == "round" else "lerp"
-    jobs = []
+    jobs, keys = [], []
     for p in range(passes):
         for l in range(layers):
             x = stack.host[l]
             got = stack.got[l] if (p == 0 and l in check_layers) else None
-            jobs.append((x["q"], x["k"], x["v"], x["dout"], float(stack.alphas[l]),
-                         stack.W, base, mode, got))
+            slabs = ([(b, h) for b in range(wl.B) for h in range(wl.H)] if per_slab
+                     else [None])
+            for bh in slabs:
+                cut = (lambda a: a) if bh is None else (
+                    lambda a, b=bh[0], h=bh[1]: a[b:b + 1, h:h + 1])
+                jobs.append((cut(x["q"]), cut(x["k"]), cut(x["v"]), cut(x["dout"]),
+                             float(stack.alphas[l]), stack.W, base, mode,
+                             None if got is None else {n: cut(a) for n, a in got.items()}))
+                keys.append((p, l))
     ctx = multiprocessing.get_context("spawn")
     from concurrent.futures import ProcessPoolExecutor
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
@@ -649,24 +660,30 @@ def cpu_baseline(stack, pattern="fib", passes=2):
         res = list(ex.map(_oracle_layer, jobs))
         wall = time.perf_counter() - t0
     th = passes * layers * wl.B * wl.H * wl.T
+    unit = "(b,h) slab" if per_slab else "layer"
     base_line = {"value": round(th / wall, 1), "unit": "tokens·heads/s",
                  "cores": workers, "kind": "oracle",
                  "sample": (f"{passes} passes over {layers} layers x {wl.B * wl.H} (b,h) "
                             f"slabs of {wl.name} (W={stack.W}), forward+backward in "
-                            f"fp64 numpy, {workers} spawned single-threaded workers; "
-                            f"{wall:.1f} s wall, {sum(r[0] for r in res):.1f} s CPU")}
+                            f"fp64 numpy, one {unit} per task, {workers} spawned "
+                            f"single-threaded workers; {wall:.1f} s wall, "
+                            f"{sum(r[0] for r in res):.1f} s CPU")}
     parity = None
     if check_layers:
         errs = {n: 0.0 for n in ("out", "lse", "dq", "dk", "dv")}
-        da_rel = 0.0
-        for l, r in zip(range(layers), res[:layers]):
-            if l not in check_layers:
+        da_parts = {l: [] for l in check_layers}
+        for (p, l), r in zip(keys, res):
+            if p != 0 or l not in check_layers:
                 continue
             for n in errs:
                 errs[n] = max(errs[n], r[1][n])
+            da_parts[l].append(r[2])
+        da_rel = 0.0
+        for l in check_layers:
+            ref = math.fsum(da_parts[l])
             got_da = stack.da[l]
-            if r[2] != 0.0:
-                da_rel = max(da_rel, abs(got_da - r[2]) / abs(r[2]))
+            if ref != 0.0:
+                da_rel = max(da_rel, abs(got_da - ref) / abs(ref))
             elif got_da != 0.0:
                 da_rel = float("inf")
         tol = TOL_MAX_ABS[wl.dtype]
@@ -744,6 +761,12 @@ def main():
                     choices=["fib", "fib-round", "pow2", "pow2-round"],
                     help="tap pattern: Fibonacci or power-of-two base, "
                          "interpolated or rounded offsets (default fib)")
+    ap.add_argument("--skip-c1", action="store_true",
+                    help="leave out the fp32 B1 H4 T256 layer (alpha = 1, W = 8)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed root of the synthetic inputs (default: the recipe's)")
+    ap.add_argument("--jsonl", default=None,
+                    help="also write one JSON record per workload to this file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (3 launches), whose "
                          "FETCH_SIZE/WRITE_SIZE counters scale the kernels' counters "
@@ -771,7 +794,7 @@ def main():
         torch.cuda.empty_cache()
 
     wl = I.WORKLOADS["linear16_bwd_bf16_b8h8t1024d64_w12"]
-    stack = Stack(wl, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
+    stack = Stack(wl, 12, args.layers, torch, F, I, args.pattern, args.out_bf16, args.seed)
     print(f"[bench] {wl.name}: {args.layers} layers resident", file=sys.stderr, flush=True)
     ms_step, per_ms, counts = time_stack(stack, args.steps, args.warmup, torch)
     value, kernels, frac, passes = summarise(stack, ms_step, per_ms)
@@ -813,7 +836,7 @@ def main():
 
     if not args.skip_t4096:
         wl2 = I.WORKLOADS["coprime16_bf16_b4h8t4096d64_w6-12"]
-        st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern, args.out_bf16)
+        st2 = Stack(wl2, 12, args.layers, torch, F, I, args.pattern, args.out_bf16, args.seed)
         print(f"[bench] {wl2.name} W=12 resident", file=sys.stderr, flush=True)
         ms2, per2, cnt2 = time_stack(st2, max(1, args.steps // 2), max(1, args.warmup), torch)
         v2, k2, f2, p2 = summarise(st2, ms2, per2)
@@ -852,7 +875,7 @@ def main():
 
     if not args.skip_t65536:
         wl4 = I.WORKLOADS["linear16_bf16_b1h16t65536d128_w12"]
-        st4 = Stack(wl4, 12, 1, torch, F, I, args.pattern, args.out_bf16)
+        st4 = Stack(wl4, 12, 1, torch, F, I, args.pattern, args.out_bf16, args.seed)
         print(f"[bench] {wl4.name} (one layer) resident", file=sys.stderr, flush=True)
         ms4, per4, cnt4 = time_stack(st4, max(2, args.steps // 2), 1, torch)
         v4, k4, f4, p4 = summarise(st4, ms4, per4)
@@ -860,7 +883,24 @@ def main():
                          "value": round(v4, 1), "ms_per_step": round(ms4, 4),
                          "consistency": consistency(ms4, per4, cnt4),
                          "hbm_frac": f4, "pass_tokens_heads_per_s": p4, "kernels": k4}
+        # every head of the layer, for the oracle check after the GPU legs
+        snap65536 = st4.snapshot((0,)) if not args.no_cpu_baseline else None
         del st4
+        torch.cuda.empty_cache()
+
+    if not args.skip_c1:
+        # the fp32 layer: alpha = 1, integer offsets, the lane-per-row kernels
+        wl1 = I.WORKLOADS["fixed_f32_b1h4t256d64_w8"]
+        st1 = Stack(wl1, 8, 1, torch, F, I, args.pattern, False, args.seed)
+        print(f"[bench] {wl1.name} resident", file=sys.stderr, flush=True)
+        ms1, per1, cnt1 = time_stack(st1, max(20, args.steps * 5), max(5, args.warmup), torch)
+        v1, k1, f1, p1 = summarise(st1, ms1, per1)
+        res["c1"] = {"workload": wl1.name + " (one layer, alpha = 1, W = 8, fp32)",
+                     "value": round(v1, 1), "ms_per_step": round(ms1, 4),
+                     "consistency": consistency(ms1, per1, cnt1), "hbm_frac": f1,
+                     "pass_tokens_heads_per_s": p1, "kernels": k1}
+        snap_c1 = st1.snapshot((0,)) if not args.no_cpu_baseline else None
+        del st1
         torch.cuda.empty_cache()
 
     if not args.skip_decode:
@@ -925,9 +965,39 @@ def main():
             cb, par = cpu_baseline(snap4096, args.pattern, passes=1)
             res["t4096"]["cpu_baseline"] = cb
             res["t4096"]["parity"] = par
+        if not args.skip_t65536:
+            cb, par = cpu_baseline(snap65536, args.pattern, passes=1, per_slab=True)
+            res["t65536"]["cpu_baseline"] = cb
+            res["t65536"]["parity"] = par
+        if not args.skip_c1:
+            cb, par = cpu_baseline(snap_c1, args.pattern, passes=20)
+            res["c1"]["cpu_baseline"] = cb
+            res["c1"]["parity"] = par
     else:
         res["cpu_baseline"] = None
+    res["seed_root"] = I.SEED_ROOT if args.seed is None else args.seed
+    if args.jsonl:
+        write_jsonl(args.jsonl, res)
     print(json.dumps(res), flush=True)
+
+
+def write_jsonl(path, res):
+    """One record per workload of the run (the configurations and the other
+    legs), each with the run's seed root, appended to `path`."""
+    main_keys = ("workload", "value", "ms_per_step", "roofline", "consistency",
+                 "hbm_frac", "pass_tokens_heads_per_s", "kernels", "parity",
+                 "cpu_baseline")
+    head = {k: res[k] for k in main_keys if k in res}
+    head["workload"] = res["config"]["workload"]
+    records = [("C2+C4 forward+backward", head)]
+    for key, label in (("c1", "C1"), ("t4096", "C3 forward+backward"),
+                       ("t65536", "C5 forward+backward, one layer"), ("decode", "decoding step"),
+                       ("learned", "learned alpha step"), ("rope", "RoPE")):
+        if key in res:
+            records.append((label, res[key]))
+    with open(path, "a") as fh:
+        for label, rec in records:
+            fh.write(json.dumps({"record": label, "seed_root": res["seed_root"], **rec}) + "\n")
 
 
 if __name__ == "__main__":

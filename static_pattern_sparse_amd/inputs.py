@@ -6,9 +6,10 @@ the HIP path and the CPU checker can both consume what it returns.
 Recipe (the same for every workload):
 
 * q, k, v and the upstream gradient dout are i.i.d. N(0, 1), drawn in float64
-  from numpy's PCG64 seeded with SeedSequence([20260630, workload_id, layer,
+  from numpy's PCG64 seeded with SeedSequence([seed_root, workload_id, layer,
   tensor_id]) with tensor_id q=0, k=1, v=2, dout=3, one (b, h) slab after the
-  other in row-major [B, H, T, D] order.
+  other in row-major [B, H, T, D] order; seed_root is 20260630 unless a caller
+  asks for another draw.
 * q and k are then rotated by RoPE at positions 0..T-1 ("rotate-half" pairing
   (m, m + D/2), angle p * base**(-2m/D)), still in float64: the attention
   layer applies RoPE before its gather [Depth-Staggered Fibonacci Spacing for
@@ -69,8 +70,9 @@ WORKLOADS = {w.name: w for w in [
 DECODE_CACHES = 4
 
 
-def _rng(workload_id: int, layer: int, tensor: str) -> np.random.Generator:
-    ss = np.random.SeedSequence([SEED_ROOT, int(workload_id), int(layer),
+def _rng(workload_id: int, layer: int, tensor: str,
+         seed_root: int = SEED_ROOT) -> np.random.Generator:
+    ss = np.random.SeedSequence([int(seed_root), int(workload_id), int(layer),
                                  TENSOR_IDS[tensor]])
     return np.random.Generator(np.random.PCG64(ss))
 
@@ -102,9 +104,10 @@ def _rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
     return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
 
 
-def make_tensor(B, H, T, D, dtype, workload_id, layer, tensor, rope_base=None):
+def make_tensor(B, H, T, D, dtype, workload_id, layer, tensor, rope_base=None,
+                seed_root=SEED_ROOT):
     """One input tensor [B, H, T, D] as float32 holding dtype-exact values."""
-    rng = _rng(workload_id, layer, tensor)
+    rng = _rng(workload_id, layer, tensor, seed_root)
     out = np.empty((B, H, T, D), dtype=np.float32)
     tabs = rope_tables(T, D, rope_base) if rope_base is not None else None
     for b in range(B):
@@ -118,21 +121,21 @@ def make_tensor(B, H, T, D, dtype, workload_id, layer, tensor, rope_base=None):
 
 
 def make_inputs(B, H, T, D, dtype, workload_id, layer, rope_base=10000.0,
-                with_dout=True):
+                with_dout=True, seed_root=SEED_ROOT):
     """q, k (post-RoPE), v and optionally dout for one layer."""
     res = {}
     for name in ("q", "k", "v") + (("dout",) if with_dout else ()):
         base = rope_base if name in ("q", "k") else None
         res[name] = make_tensor(B, H, T, D, dtype, workload_id, layer, name,
-                                base)
+                                base, seed_root)
     return res
 
 
-def workload_inputs(w: Workload, layer: int, with_dout=None):
+def workload_inputs(w: Workload, layer: int, with_dout=None, seed_root=SEED_ROOT):
     if with_dout is None:
         with_dout = True
     return make_inputs(w.B, w.H, w.T, w.D, w.dtype, w.workload_id, layer,
-                       w.rope_base, with_dout)
+                       w.rope_base, with_dout, seed_root)
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda"):

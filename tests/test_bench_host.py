@@ -109,3 +109,52 @@ def test_event_pairs_time_each_launch_alone():
     med, counts = ev.per_kernel_ms(skip_steps=1)
     assert counts == {"fwd": 3, "bwd": 3}
     assert abs(med["fwd"] - 1.0) < 1e-12 and abs(med["bwd"] - 2.5) < 1e-12
+
+
+def test_jsonl_records_every_workload(tmp_path):
+    """write_jsonl appends one record per workload of the run, each carrying
+    the seed root, the main step under the C2+C4 label."""
+    import json
+    res = {"config": {"workload": "linear16"}, "value": 1.0, "ms_per_step": 2.0,
+           "roofline": {"frac": 0.3}, "parity": {"ok": True}, "seed_root": 7,
+           "c1": {"workload": "fixed", "value": 3.0}, "t4096": {"workload": "coprime"},
+           "t65536": {"workload": "long"}, "decode": {"workload": "dec"}}
+    path = tmp_path / "runs.jsonl"
+    bench.write_jsonl(str(path), res)
+    bench.write_jsonl(str(path), res)
+    recs = [json.loads(l) for l in path.read_text().splitlines()]
+    assert len(recs) == 10
+    labels = [r["record"] for r in recs[:5]]
+    assert labels == ["C2+C4 forward+backward", "C1", "C3 forward+backward",
+                      "C5 forward+backward, one layer", "decoding step"]
+    assert recs[0]["workload"] == "linear16" and recs[0]["roofline"] == {"frac": 0.3}
+    assert all(r["seed_root"] == 7 for r in recs)
+
+
+def test_oracle_baseline_per_slab_matches_per_layer():
+    """The per-slab oracle tasks of a long layer give the same parity verdict
+    and dalpha as one task per layer (a tiny stack, CPU only)."""
+    import types
+    import numpy as np
+    from static_pattern_sparse_amd import inputs as I
+    from oracle import fsa_oracle as O
+    B, H, T, D, W, a = 1, 2, 48, 16, 4, 0.7317
+    x = I.make_inputs(B, H, T, D, "f32", 77, 0)
+    got = {n: np.zeros((B, H, T, D), np.float32) for n in ("out", "dq", "dk", "dv")}
+    got["lse"] = np.zeros((B, H, T), np.float32)
+    da = 0.0
+    for h in range(H):
+        sl = [x[n][0, h].astype(np.float64) for n in ("q", "k", "v", "dout")]
+        o, l = O.forward_slab(sl[0], sl[1], sl[2], a, W)
+        dq, dk, dv, dalpha, _ = O.backward_slab(sl[0], sl[1], sl[2], sl[3], a, W)
+        got["out"][0, h], got["lse"][0, h] = o, l
+        got["dq"][0, h], got["dk"][0, h], got["dv"][0, h] = dq, dk, dv
+        da += dalpha
+    wl = types.SimpleNamespace(name="tiny", B=B, H=H, T=T, dtype="f32")
+    snap = types.SimpleNamespace(wl=wl, layers=1, W=W, alphas=[a], out_bytes=4,
+                                 host=[x], got={0: got}, da={0: da})
+    _, p1 = bench.cpu_baseline(snap, passes=1)
+    _, p2 = bench.cpu_baseline(snap, passes=1, per_slab=True)
+    assert p1["ok"] and p2["ok"]
+    assert p1["max_abs"] == p2["max_abs"]
+    assert p2["dalpha_rel"] <= 1e-12

@@ -59,3 +59,15 @@ def test_decode_inputs_share_the_sequence_generator():
     xb = I.make_decode_inputs(2, 1, 50, 64, "bf16", 9, 1, [49, 0])
     for t in (xb["q"], xb["k"], xb["v"]):
         assert np.array_equal(t, I.round_to_bf16(t))       # bf16-exact
+
+
+def test_seed_root_gives_another_draw_and_defaults_to_the_recipe():
+    """The default seed root is the recipe's; another root is another draw of
+    the same shapes and rounding."""
+    a = I.make_inputs(1, 2, 64, 16, "bf16", 2, 3)
+    b = I.make_inputs(1, 2, 64, 16, "bf16", 2, 3, seed_root=I.SEED_ROOT)
+    c = I.make_inputs(1, 2, 64, 16, "bf16", 2, 3, seed_root=I.SEED_ROOT + 1)
+    for n in ("q", "k", "v", "dout"):
+        assert np.array_equal(a[n], b[n])
+        assert not np.array_equal(a[n], c[n])
+        assert np.array_equal(c[n], I.round_to_bf16(c[n]))
