@@ -843,8 +843,9 @@ __global__ __launch_bounds__(64) void fwd_mfma_kernel(
 //   -f * [dS * scale * q.(K[a+1]-K[a]) + p * dout.(V[a+1]-V[a])]
 // = A - Delta_i * B with A and B accumulated per lane. The wavefront writes
 // Delta_i, dq, and one dalpha partial.
+// Register budget: five wavefronts per SIMD at D = 64 (96 VGPRs).
 template <int D, bool kRope>
-__global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 5 : 1))) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, Problem pr, TapsArg taps_arg, int n_tiles, int hg,
@@ -868,7 +869,6 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   const rsrc_t rg = make_rsrc(dout + base, slab);
   const Slab sk{k + base, slab}, sv{v + base, slab};
   const TileLane<D> tl = tile_lane<D>(lane);
-  const TapLane tv = tap_lane(taps);
   const int i = i0 + n;
   const bool qvalid = n < kTileQ && i < T;
   const float scale = pr.scale;
@@ -879,7 +879,8 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   // is the causal one), none wholly before row 0
   const int nwb = min((min(W, T) + kTileQ - 1) / 16 + 1, (i0 + 15) / 16 + 1);
   const int nwp = (nwb + 1) / 2;
-  const int ntap = taps_upto(tv, taps.n, lane, min(i0 + kTileQ - 1, T - 1));
+  int ntap = 0;                                         // taps some query reaches
+  while (ntap < taps.n && taps.c[ntap] <= min(i0 + kTileQ - 1, T - 1)) ++ntap;
 
   zero_lds(lds, kStage, lane);
   __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -922,16 +923,19 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
         dwin += pe * d[j];
       }
     }
-    u32x4 h1, l1, h2, l2;
-    split8(w1, &h1, &l1);
-    split8(w2, &h2, &l2);
+    // K^T (P o dP) first, then K^T P: one pair of hi/lo operands live at a time
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb) {
-      const u32x4 a = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
-      a1[mb] = mfma(a, h1, a1[mb]);
-      a1[mb] = mfma(a, l1, a1[mb]);
-      a2[mb] = mfma(a, h2, a2[mb]);
-      a2[mb] = mfma(a, l2, a2[mb]);
+    for (int part = 0; part < 2; ++part) {
+      u32x4 hi, lo;
+      split8(part ? w2 : w1, &hi, &lo);
+      f32x4* acc = part ? a2 : a1;
+#pragma unroll
+      for (int mb = 0; mb < D / 16; ++mb) {
+        const u32x4 a = tr_operand<D>(lds, lds + Tl::kBlockBytes, tl, mb);
+        acc[mb] = mfma(a, hi, acc[mb]);
+        acc[mb] = mfma(a, lo, acc[mb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
@@ -945,10 +949,12 @@ __global__ __launch_bounds__(64) void bwd_dq_mfma_kernel(
   for (int tp = 0; 2 * tp < ntap; ++tp) {
     const int t0 = 2 * tp, t1 = t0 + 1;
     const bool has1 = t1 < ntap;
-    const int c0 = rl_i(tv.c, t0), c1 = rl_i(tv.c, t1);
-    const float wl0 = rl_f(tv.wl, t0), wh0 = rl_f(tv.wh, t0);
-    const float wl1 = rl_f(tv.wl, t1), wh1 = rl_f(tv.wh, t1);
-    const float nf0 = rl_f(tv.nf, t0), nf1 = rl_f(tv.nf, t1);
+    // tap constants by scalar loads from the table (no lanes held for them)
+    const int t1c = min(t1, kNumTaps - 1);
+    const int c0 = taps.c[t0], c1 = taps.c[t1c];
+    const float wl0 = taps.w_lo[t0], wh0 = taps.w_hi[t0];
+    const float wl1 = taps.w_lo[t1c], wh1 = taps.w_hi[t1c];
+    const float nf0 = taps.neg_f[t0], nf1 = taps.neg_f[t1c];
     stage_two<D>(sk, sv, tl, i0 - c0, has1 ? i0 - c1 : INT_MIN, lds);
     wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
