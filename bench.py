@@ -889,7 +889,7 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.skip_c1:
-        # the fp32 layer: alpha = 1, integer offsets, the lane-per-row kernels
+        # the fp32 layer: alpha = 1, integer offsets, the row-group kernels
         wl1 = I.WORKLOADS["fixed_f32_b1h4t256d64_w8"]
         st1 = Stack(wl1, 8, 1, torch, F, I, args.pattern, False, args.seed)
         print(f"[bench] {wl1.name} resident", file=sys.stderr, flush=True)

@@ -45,7 +45,7 @@ int check_shape(int dtype, int B, int H, int T, int D, float alpha, int window) 
     return FSA_ERR_INVALID_ARG;
   if (dtype != FSA_DTYPE_F32 && dtype != FSA_DTYPE_BF16) return FSA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return FSA_ERR_UNSUPPORTED;
-  // grid limits: heads on grid.y of the lane-per-row kernels, one tile per
+  // grid limits: heads on grid.y of the row-group kernels, one tile per
   // workgroup on grid.x of the tile kernels
   if (static_cast<long long>(B) * H > 65535) return FSA_ERR_UNSUPPORTED;
   if ((static_cast<long long>(T) + 13) / 14 * B * H > 0x7fffffffLL)
@@ -136,7 +136,7 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int T, int D, int dtype) {
 }
 
 // Kernel family: bf16 inputs take the MFMA tile kernels, fp32 inputs the
-// lane-per-row kernels.
+// row-group kernels.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const TapsArg& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s) {

@@ -86,7 +86,7 @@ int backward_both(const void* q, const void* k, const void* v, const void* dout,
                   size_t workspace_bytes, void* stream);
 
 // Launchers; each returns the hipError_t of its launch. The kernel family is
-// chosen from dtype: fp32 inputs use the lane-per-row kernels, bf16 inputs the
+// chosen from dtype: fp32 inputs use the row-group kernels, bf16 inputs the
 // MFMA tile kernels. `out` is fp32, or bf16 (round to nearest even) when
 // out_bf16.
 hipError_t launch_forward(const void* q, const void* k, const void* v,
@@ -123,7 +123,7 @@ hipError_t launch_rope(const void* x, int in_dtype, int B, int H, int T, int D,
 // workgroups the pass launches (the 1-D grid must stay below 2^31)
 long long rope_blocks(int B, int H, int T, int D);
 
-// lane-per-row kernels (fsa_vec.hip)
+// row-group kernels (fsa_vec.hip): eight lanes per row
 hipError_t launch_fwd_vec(const void* q, const void* k, const void* v,
                           int dtype, const Problem& pr, const TapsArg& taps,
                           void* out, bool out_bf16, float* lse, hipStream_t s);

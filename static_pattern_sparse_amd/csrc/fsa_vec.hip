@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kVecBlock) void bwd_dq_vec_kernel(
     store_part<D>(dq + base + static_cast<size_t>(i) * D, e, o);
     if (e == 0) {
       delta[static_cast<size_t>(blockIdx.y) * T + i] = Dsum;
-      dal = al_a - Dsum * al_b;                 // one lane per row contributes
+      dal = al_a - Dsum * al_b;                 // one lane of the group contributes
     }
   }
   // fixed-order wavefront reduction of the alpha gradient

@@ -228,7 +228,7 @@ def test_sharp_scores(dtype, qscale, alpha, W):
     """q scaled by a power of two (exact in both dtypes): scores of tens of
     units, so the softmax is dominated by a few entries and the running max
     moves often and far (the lazy rescale of the tile kernels and the online
-    max of the lane-per-row kernels)."""
+    max of the row-group kernels)."""
     _say("sharp scores", dtype, qscale, alpha, W)
     alpha = float(np.float32(alpha))
     x = _rand_inputs(2, 2, 900, 64, dtype, 40 + int(qscale))
@@ -334,7 +334,7 @@ def test_workload_long_t65536_full(layer):
 
 # ------------------------------------------------------------------ bf16 output
 BF16_OUT_CASES = [
-    # B, H, T, D, dtype, alpha, W  (bf16: tile kernels; f32: lane-per-row kernels)
+    # B, H, T, D, dtype, alpha, W  (bf16: tile kernels; f32: row-group kernels)
     (2, 2, 700, 64, "bf16", 0.7317, 12),
     (1, 2, 333, 128, "bf16", 1.2913, 6),
     (1, 1, 300, 64, "f32", 0.9, 5),
