@@ -84,10 +84,10 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int n_tiles, int* bh,
 // and V rows fit in half of the XCD's L2: the longest tiles of all the
 // group's heads then start first, and when every tile of a launch is
 // resident at once they no longer end last (forward 15.9 -> 14.9 us at
-// B8 H8 T1024, hg = 8; unchanged at B4 H8 T4096, hg = 2). dq takes pairs of
-// heads (21.8 -> 21.3 us at T1024, unchanged at T4096; groups of 4 and 8
-// measured slower); the key-side kernel keeps map_tile's order, which
-// measured fastest for it.
+// B8 H8 T1024, hg = 8; unchanged at B4 H8 T4096, hg = 2). dq takes the same
+// groups (20.0 -> 19.5 us at T1024 against pairs of heads, unchanged at
+// T4096); the key-side kernel keeps map_tile's order, which measured
+// fastest for it.
 __device__ __forceinline__ void map_tile_grouped(int bid, int BH, int n_tiles, int hg,
                                                  int* bh, int* tile) {
   if ((BH & 7) == 0 && hg > 1) {
@@ -1349,7 +1349,7 @@ hipError_t launch_bwd_dq_mfma(const void* q, const void* k, const void* v,
                               const RopeArg& rope) {
   const int n_tiles = (pr.T + kTileQ - 1) / kTileQ;
   const dim3 grid(n_tiles * pr.B * pr.H);
-  const int hg = head_group(pr, 2);
+  const int hg = head_group(pr, 8);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
