@@ -136,8 +136,9 @@ SMALL = [
     (2, 1, 500, 128, "bf16", 1.1, 100),
     (1, 2, 300, 64, "bf16", 0.9, 5000),         # W far past T: causal attention
     (2, 1, 29, 64, "bf16", 1.1, 2),
-    # B*H a multiple of 8 with a partial last head group per XCD: dq pairs
-    # heads over 3 heads per XCD; the forward groups 3 over 5 heads per XCD
+    # B*H a multiple of 8, so that the query-side kernels group heads per XCD:
+    # 3 heads per XCD in one group at T1000; 5 heads per XCD at T2050, where
+    # half the L2 holds 3 heads' K and V, in a group of 3 and a partial one of 2
     (3, 8, 1000, 64, "bf16", 0.7317, 12),
     (5, 8, 2050, 64, "bf16", 1.2913, 10),
 ]
