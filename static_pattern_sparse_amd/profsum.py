@@ -111,6 +111,7 @@ BENCH_LAUNCHES = {
 
 L2_LINE = 128          # bytes per L1 -> L2 read request (one L2 line)
 N_CU = 256
+L2_CHANNELS = 128      # 16 per XCD
 
 
 def _counters(paths):
@@ -134,7 +135,9 @@ def counter_metrics(paths):
                               over the 8 XCDs)
       tcp_pending_stall       TCP_PENDING_STALL_CYCLES per L1, the same
                               fraction (the L1 stalled on misses in flight)
-      ta_busy                 TA_BUSY_avr, the same fraction"""
+      ta_busy                 TA_BUSY_avr, the same fraction
+      l2_tag_stall            TCC_TAG_STALL per L2 channel (16 per XCD), the
+                              same fraction"""
     c = _counters(paths)
     out = {}
     for key, d in c.items():
@@ -155,6 +158,8 @@ def counter_metrics(paths):
             m["tcp_pending_stall"] = d["TCP_PENDING_STALL_CYCLES_sum"] / N_CU / (d["GRBM_GUI_ACTIVE"] / 8.0)
         if d.get("GRBM_GUI_ACTIVE") and d.get("TA_BUSY_avr") is not None:
             m["ta_busy"] = d["TA_BUSY_avr"] / (d["GRBM_GUI_ACTIVE"] / 8.0)
+        if d.get("GRBM_GUI_ACTIVE") and d.get("TCC_TAG_STALL_sum") is not None:
+            m["l2_tag_stall"] = d["TCC_TAG_STALL_sum"] / L2_CHANNELS / (d["GRBM_GUI_ACTIVE"] / 8.0)
         out[key] = m
     return out
 
