@@ -137,7 +137,10 @@ def counter_metrics(paths):
                               fraction (the L1 stalled on misses in flight)
       ta_busy                 TA_BUSY_avr, the same fraction
       l2_tag_stall            TCC_TAG_STALL per L2 channel (16 per XCD), the
-                              same fraction"""
+                              same fraction
+      l2_busy                 TCC_BUSY_avr, the same fraction (a channel with
+                              requests in flight)
+      l2_req_per_channel_cycle  TCC_REQ per channel per cycle"""
     c = _counters(paths)
     out = {}
     for key, d in c.items():
@@ -160,6 +163,10 @@ def counter_metrics(paths):
             m["ta_busy"] = d["TA_BUSY_avr"] / (d["GRBM_GUI_ACTIVE"] / 8.0)
         if d.get("GRBM_GUI_ACTIVE") and d.get("TCC_TAG_STALL_sum") is not None:
             m["l2_tag_stall"] = d["TCC_TAG_STALL_sum"] / L2_CHANNELS / (d["GRBM_GUI_ACTIVE"] / 8.0)
+        if d.get("GRBM_GUI_ACTIVE") and d.get("TCC_BUSY_avr") is not None:
+            m["l2_busy"] = d["TCC_BUSY_avr"] / (d["GRBM_GUI_ACTIVE"] / 8.0)
+        if d.get("GRBM_GUI_ACTIVE") and d.get("TCC_REQ_sum") is not None:
+            m["l2_req_per_channel_cycle"] = d["TCC_REQ_sum"] / L2_CHANNELS / (d["GRBM_GUI_ACTIVE"] / 8.0)
         out[key] = m
     return out
 
