@@ -87,6 +87,7 @@ def test_counter_metrics(tmp_path):
         ("TCP_PENDING_STALL_CYCLES_sum", 256 * 200.0),
         ("TA_BUSY_avr", 300.0),
         ("TCC_TAG_STALL_sum", 128 * 50.0),
+        ("TCC_BUSY_avr", 700.0), ("TCC_REQ_sum", 128 * 250.0),
     ]
     a = _counter_csv(tmp_path / "a.csv", [(FWD, 4416, c, v) for c, v in rows[:5]])
     b = _counter_csv(tmp_path / "b.csv", [(FWD, 4416, c, v) for c, v in rows[4:]]
@@ -102,3 +103,4 @@ def test_counter_metrics(tmp_path):
     assert x["tcp_pending_stall"] == 0.2
     assert x["ta_busy"] == 0.3
     assert x["l2_tag_stall"] == 0.05
+    assert x["l2_busy"] == 0.7 and x["l2_req_per_channel_cycle"] == 0.25
